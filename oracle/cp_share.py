@@ -1,0 +1,85 @@
+"""Per-rank shares of context-parallel attention, composed from the oracle's steps.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Two layouts, from [vllm-omni#7641] (commit message):
+
+* AllGather-KV over A ranks: rank r keeps query rows ``[r*S/A, (r+1)*S/A)`` and
+  attends to the gathered global K/V of all heads.
+* 2D, Ulysses degree U times AllGather-KV degree A (ring degree 1): global rank
+  ``g = a*U + u``.  Ulysses groups are contiguous blocks of U ranks
+  (group a = ranks ``a*U .. a*U+U-1``); AllGather-KV groups stride by U
+  (group u = ranks ``u, u+U, u+2U, ...``).  Rank g starts with rows
+  ``[g*S_l, (g+1)*S_l)``, ``S_l = S/(U*A)``, of all heads.  The Ulysses exchange
+  inside group a leaves rank (a, u) with region a (rows ``[a*S/A, (a+1)*S/A)``) of
+  heads ``[u*H/U, (u+1)*H/U)``; the K/V all-gather inside group u, in rank order,
+  rebuilds every region of those heads in sequence order; attention is then a
+  plain local-Q/global-KV problem; the reverse Ulysses step returns rank g's own
+  rows with all heads.
+
+The functions return every rank's result so that tests can check that the ranks'
+outputs, concatenated in global rank order, equal single-rank attention.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import attention as _attn
+from . import layout as _layout
+
+
+def agkv_outputs(q_full, k_full, v_full, A, key_mask=None, scale=None):
+    """Rank r of A: ``attention(Q rows of region r, all K, all V)``; list over ranks."""
+    S = q_full.shape[1]
+    if S % A:
+        raise ValueError("S must divide by A")
+    Sl = S // A
+    return [_attn.attention(q_full[:, r * Sl:(r + 1) * Sl], k_full, v_full, key_mask, scale)
+            for r in range(A)]
+
+
+def ulysses_groups(U, A):
+    return [[a * U + u for u in range(U)] for a in range(A)]
+
+
+def agkv_groups(U, A):
+    return [[u + k * U for k in range(A)] for u in range(U)]
+
+
+def composed_2d(q_full, k_full, v_full, U, A, key_mask=None, scale=None):
+    """Run the 2D layout on every rank.
+
+    Returns ``(attn_inputs, outputs)``: ``attn_inputs[g] = (q, k, v)`` is the
+    local-Q/global-KV problem rank g hands to attention, and ``outputs[g]`` is rank
+    g's final ``[B, S_l, H, D]`` output after the reverse exchange.
+    """
+    B, S, H, D = q_full.shape
+    P = U * A
+    if S % P or H % U:
+        raise ValueError("S must divide by U*A and H by U")
+    Sl = S // P
+    shard = [tuple(t[:, g * Sl:(g + 1) * Sl] for t in (q_full, k_full, v_full))
+             for g in range(P)]
+
+    after_ulysses = [None] * P
+    for group in ulysses_groups(U, A):
+        res = _layout.ulysses_forward([shard[g] for g in group], U)
+        for u, g in enumerate(group):
+            after_ulysses[g] = res[u]
+
+    attn_inputs = [None] * P
+    for group in agkv_groups(U, A):
+        k_all = np.concatenate([after_ulysses[g][1] for g in group], axis=1)
+        v_all = np.concatenate([after_ulysses[g][2] for g in group], axis=1)
+        for g in group:
+            attn_inputs[g] = (after_ulysses[g][0], k_all, v_all)
+
+    o_hs = [_attn.attention(*attn_inputs[g], key_mask=key_mask, scale=scale) for g in range(P)]
+
+    outputs = [None] * P
+    for group in ulysses_groups(U, A):
+        res = _layout.ulysses_reverse([o_hs[g] for g in group], U)
+        for u, g in enumerate(group):
+            outputs[g] = res[u]
+    return attn_inputs, outputs

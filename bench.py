@@ -1,0 +1,416 @@
+#!/usr/bin/env python3
+"""Benchmark of one rank's share of context-parallel diffusion attention on one GPU.
+
+One step = one pass of the whole per-rank hot path for global rank 0 of the
+chosen workload, with every input resident in HBM:
+
+  1. cp_pack_qkv_dst_major   this rank's Q/K/V shard -> its staging buffer
+  2. cp_sim_exchange         receive chunk 0 of every group member's staging buffer
+                             (the other members' buffers are resident inputs,
+                             packed before timing: they stand in for the peers)
+  3. cp_unpack_head_sharded  -> head-sharded Q/K/V
+  4. cp_attn_localq_globalkv the workload's local-Q/global-KV attention
+  5. cp_output_reverse       send layout (B > 1 only; the identity for B == 1),
+     cp_sim_exchange         exchange with the peers' resident send buffers,
+     cp_output_reverse       merge of the W head groups
+
+For the 2D workload (video_u2a2: Ulysses U=2 x AllGather-KV A=2) the steps chain:
+step 3 writes K/V straight into region 0 of the gathered global K/V buffer
+(region 1, the other AllGather rank's share, is resident), step 4 attends the
+unpacked Q against it, and step 5 reverses its output.  For the AllGather-KV
+workloads (tiny_w2, image_cp4, image_cp8, joint_cfg_cp4) the attention reads the
+rank's local Q shard against the resident global K/V (standing in for the K/V
+all-gather), and the output reverse runs on a resident head-sharded buffer of the
+Ulysses layout.
+
+Prints one JSON line.  `value` is attention TFLOP/s over the whole step
+(algorithmic attention FLOPs / step time); per-kernel durations come from HIP
+events recorded around each launch on the launch stream.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn TFLOP/s + % bf16 MFMA peak (local-Q/global-KV); pack/unpack HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+DEFAULT_WORKLOAD = "image_cp4"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=10.0)
+    p.add_argument("--no-cold", action="store_true", help="skip the cold-cache pack/unpack pass")
+    p.add_argument("--only", default=None,
+                   help="profile aid: run only this kernel's launches in the timed loop "
+                        "(pack|unpack|attn|merge); the JSON line is then not the headline")
+    return p.parse_args()
+
+
+def to_dev(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+class RankPath:
+    """Device buffers and launches of one rank's step."""
+
+    def __init__(self, wl, dev):
+        import torch
+
+        import context_attention_diffusion_amd as cp
+        import workloads
+
+        self.cp, self.wl, self.dev = cp, wl, dev
+        W, B, Sl, H, D, A = wl.W, wl.B, wl.S_local, wl.H, wl.D, wl.A
+        Hl = H // W
+        self.two_d = A > 1
+        full = workloads.global_qkv(wl)
+        # Ulysses group 0: ranks 0..W-1 with rows [r*S_l, (r+1)*S_l).
+        shards = [[to_dev(np.ascontiguousarray(t[:, r * Sl:(r + 1) * Sl]), dev) for t in full]
+                  for r in range(W)]
+        self.q, self.k, self.v = shards[0]
+        st_shape = (W, B * Sl, Hl, 3 * D)
+        self.staging = [torch.empty(st_shape, dtype=torch.bfloat16, device=dev) for _ in range(W)]
+        for r in range(1, W):      # peers' sends: resident inputs
+            cp.cp_pack_qkv_dst_major(*shards[r], W, staging=self.staging[r])
+        self.recv = torch.empty(st_shape, dtype=torch.bfloat16, device=dev)
+        hs_shape = (B, W * Sl, Hl, D)
+        self.q_hs = torch.empty(hs_shape, dtype=torch.bfloat16, device=dev)
+        mask = workloads.key_mask(wl)
+        self.mask = None if mask is None else torch.from_numpy(mask).to(dev)
+        if self.two_d:
+            assert B == 1
+            # Gathered K/V of heads [0, H_l): region 0 comes from step 3, region 1 is resident.
+            kg = np.ascontiguousarray(full[1][:, :, :Hl])
+            vg = np.ascontiguousarray(full[2][:, :, :Hl])
+            self.k_glob, self.v_glob = to_dev(kg, dev), to_dev(vg, dev)
+            span = W * Sl
+            self.k_hs = self.k_glob[:, :span]
+            self.v_hs = self.v_glob[:, :span]
+            self.attn_q, self.attn_k, self.attn_v = self.q_hs, self.k_glob, self.v_glob
+            self.o_attn = torch.empty(hs_shape, dtype=torch.bfloat16, device=dev)
+            self.o_hs = self.o_attn
+        else:
+            self.k_hs = torch.empty(hs_shape, dtype=torch.bfloat16, device=dev)
+            self.v_hs = torch.empty(hs_shape, dtype=torch.bfloat16, device=dev)
+            self.attn_q = self.q
+            self.attn_k = to_dev(full[1][:, :, :wl.attn_heads], dev)
+            self.attn_v = to_dev(full[2][:, :, :wl.attn_heads], dev)
+            self.o_attn = torch.empty_like(self.attn_q)
+            g = torch.Generator(device="cpu").manual_seed(wl.seed + 99)
+            self.o_hs = torch.randn(hs_shape, generator=g).to(torch.bfloat16).to(dev)
+        self.scale = 1.0 / math.sqrt(D)
+        snd_shape = (W, B, Sl, Hl, D)
+        self.snd = torch.empty(snd_shape, dtype=torch.bfloat16, device=dev)
+        g = torch.Generator(device="cpu").manual_seed(wl.seed + 7)
+        self.peer_snd = [None] + [torch.randn(snd_shape, generator=g).to(torch.bfloat16).to(dev)
+                                  for _ in range(1, W)]
+        self.rcv = torch.empty(snd_shape, dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((B, Sl, H, D), dtype=torch.bfloat16, device=dev)
+        self.full = full
+        self.mask_np = mask
+
+    # -- the launches of one step
+    def pack(self):
+        self.cp.cp_pack_qkv_dst_major(self.q, self.k, self.v, self.wl.W, staging=self.staging[0])
+
+    def exchange_in(self):
+        self.cp.cp_sim_exchange(self.staging, 0, recv=self.recv)
+
+    def unpack(self):
+        self.cp.cp_unpack_head_sharded(self.recv, self.wl.B, self.wl.W,
+                                       out=(self.q_hs, self.k_hs, self.v_hs))
+
+    def attn(self):
+        self.cp.cp_attn_localq_globalkv(self.attn_q, self.attn_k, self.attn_v, self.mask,
+                                        scale=self.scale, out=self.o_attn)
+
+    def send(self):
+        W, B = self.wl.W, self.wl.B
+        if B == 1:
+            return self.o_hs.view(self.snd.shape)     # identity layout
+        return self.cp.cp_output_reverse(0, self.o_hs, W, B, out=self.snd)
+
+    def exchange_out(self, snd):
+        self.cp.cp_sim_exchange([snd] + self.peer_snd[1:], 0, recv=self.rcv)
+
+    def merge(self):
+        self.cp.cp_output_reverse(1, self.rcv, self.wl.W, self.wl.B, out=self.out)
+
+
+def attn_flops(wl, mask):
+    """Algorithmic attention FLOPs: 4*B*H*Sq*D*(valid keys per batch)."""
+    if mask is None:
+        return wl.attn_flops_dense()
+    valid = mask.astype(np.int64).sum(axis=1)
+    return int(4 * wl.attn_heads * wl.attn_rows * wl.D * valid.sum())
+
+
+def run_steps(path, n, events=None, only=None):
+    import torch
+    names = ["pack", "exchange_in", "unpack", "attn", "send", "exchange_out", "merge"]
+    for _ in range(n):
+        rec = {} if events is not None else None
+
+        def timed(name, fn):
+            if rec is None:
+                return fn()
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            r = fn()
+            e.record()
+            rec[name] = (s, e)
+            return r
+
+        if only is None or only == "pack":
+            timed("pack", path.pack)
+        if only is None:
+            timed("exchange_in", path.exchange_in)
+        if only is None or only == "unpack":
+            timed("unpack", path.unpack)
+        if only is None or only == "attn":
+            timed("attn", path.attn)
+        if only is None:
+            snd = timed("send", path.send)
+            timed("exchange_out", lambda: path.exchange_out(snd))
+        if only is None or only == "merge":
+            timed("merge", path.merge)
+        if rec is not None:
+            events.append(rec)
+    return names
+
+
+def cold_layout_gbps(wl, dev, rounds=4):
+    """Pack and unpack with rotating buffer sets whose footprint exceeds 512 MB, so each
+    launch misses the 256 MB Infinity Cache.  Returns (pack GB/s, unpack GB/s)."""
+    import torch
+
+    import context_attention_diffusion_amd as cp
+
+    W, B, Sl, H, D = wl.W, wl.B, wl.S_local, wl.H, wl.D
+    per_set = 2 * wl.pack_bytes()
+    nsets = max(3, int(math.ceil(600e6 / per_set)))
+    sets = []
+    for i in range(nsets):
+        x = [torch.empty((B, Sl, H, D), dtype=torch.bfloat16, device=dev).normal_() for _ in range(3)]
+        st = torch.empty((W, B * Sl, H // W, 3 * D), dtype=torch.bfloat16, device=dev)
+        outs = tuple(torch.empty((B, W * Sl, H // W, D), dtype=torch.bfloat16, device=dev)
+                     for _ in range(3))
+        sets.append((x, st, outs))
+    res = []
+    for which in ("pack", "unpack"):
+        def launch(sset):
+            x, st, outs = sset
+            if which == "pack":
+                cp.cp_pack_qkv_dst_major(*x, W, staging=st)
+            else:
+                cp.cp_unpack_head_sharded(st, B, W, out=outs)
+        for sset in sets:
+            launch(sset)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(rounds):
+            for sset in sets:
+                s = torch.cuda.Event(enable_timing=True)
+                e = torch.cuda.Event(enable_timing=True)
+                s.record()
+                launch(sset)
+                e.record()
+                times.append((s, e))
+        torch.cuda.synchronize()
+        ms = float(np.median([s.elapsed_time(e) for s, e in times]))
+        res.append(wl.pack_bytes() / (ms * 1e-3) / 1e9)
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(wl, full, mask, budget_s):
+    """The oracle's attention timed on the host cores over the first n query rows of the
+    rank's problem (n sized to about budget_s of CPU work)."""
+    from oracle import attention as OA
+    from oracle import bf16
+
+    if wl.A > 1:
+        q_all = full[0][:, :wl.attn_rows, :wl.attn_heads]
+    else:
+        q_all = full[0][:, :wl.attn_rows, :wl.attn_heads]
+    k = bf16.bits_to_f64(full[1][:, :, :wl.attn_heads])
+    v = bf16.bits_to_f64(full[2][:, :, :wl.attn_heads])
+    valid = wl.S if mask is None else None
+
+    def flops(n):
+        if mask is None:
+            return 4.0 * wl.B * wl.attn_heads * n * wl.S * wl.D
+        return 4.0 * wl.attn_heads * n * wl.D * float(mask.astype(np.int64).sum())
+
+    n0 = min(wl.attn_rows, 16)
+    q0 = bf16.bits_to_f64(q_all[:, :n0])
+    t = time.perf_counter()
+    OA.attention(q0, k, v, mask, 1.0 / math.sqrt(wl.D))
+    t0 = time.perf_counter() - t
+    n = int(min(wl.attn_rows, max(n0, n0 * budget_s / max(t0, 1e-6))))
+    q = bf16.bits_to_f64(q_all[:, :n])
+    t = time.perf_counter()
+    OA.attention(q, k, v, mask, 1.0 / math.sqrt(wl.D))
+    dt = time.perf_counter() - t
+    threads = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+        info = [x for x in threadpool_info() if x.get("user_api") == "blas"]
+        if info:
+            threads = max(int(x.get("num_threads", 1)) for x in info)
+    except Exception:
+        pass
+    del valid
+    return {
+        "value": flops(n) / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"fp64 oracle attention over query rows [0,{n}) of {wl.attn_rows}, "
+                  f"{wl.attn_heads} heads, all {wl.S} keys, B={wl.B}; {dt:.1f} s; "
+                  f"host cpu_count={os.cpu_count()}",
+    }
+
+
+def parity_sample(path, wl, nrows=24):
+    """Quick parity figures for the report (the full parity suite lives in tests/)."""
+    from oracle import attention as OA
+    from oracle import bf16
+    from oracle import layout as OL
+
+    import torch
+
+    torch.cuda.synchronize()
+    res = {}
+    # unpack output vs the closed form (head slice 0 of the group's sequence)
+    Hl = wl.H // wl.W
+    span = wl.W * wl.S_local
+    got = path.q_hs.view(torch.int16).cpu().numpy().view(np.uint16)
+    res["unpack_q_bit_exact"] = bool(np.array_equal(got, path.full[0][:, :span, :Hl]))
+    del OL
+    rng = np.random.default_rng(wl.seed)
+    rows = [(int(rng.integers(wl.B)), int(rng.integers(wl.attn_rows)), int(rng.integers(wl.attn_heads)))
+            for _ in range(nrows)]
+    q = path.full[0][:, :wl.attn_rows, :wl.attn_heads]
+    ref = OA.attention_rows(bf16.bits_to_f64(q), bf16.bits_to_f64(path.full[1][:, :, :wl.attn_heads]),
+                            bf16.bits_to_f64(path.full[2][:, :, :wl.attn_heads]), rows,
+                            path.mask_np, 1.0 / math.sqrt(wl.D))
+    o = path.o_attn.float().cpu().numpy().astype(np.float64)
+    sel = np.stack([o[b, i, h] for b, i, h in rows])
+    err = np.abs(sel - ref)
+    res["attn_sampled_rows"] = nrows
+    res["attn_max_abs_err"] = float(err.max())
+    res["attn_mean_abs_err"] = float(err.mean())
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import workloads
+
+    wl = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    path = RankPath(wl, dev)
+    for _ in range(args.warmup):
+        run_steps(path, 1, only=args.only)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` steps, synchronised on both sides.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(path, args.steps, only=args.only)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # Per-kernel durations from HIP events on the launch stream, over a second pass
+    # of the same steps (the events would otherwise perturb the step clock).
+    events = []
+    run_steps(path, args.steps, events=events, only=args.only)
+    torch.cuda.synchronize()
+    kms = {}
+    for name in events[0]:
+        kms[name] = float(np.mean([rec[name][0].elapsed_time(rec[name][1]) for rec in events]))
+
+    flops = attn_flops(wl, path.mask_np)
+    pack_bytes, merge_bytes = wl.pack_bytes(), wl.merge_bytes()
+    kern = {}
+    if "attn" in kms:
+        t = kms["attn"] * 1e-3
+        kern["attn"] = {"us": kms["attn"] * 1e3, "TFLOPs": flops / t / 1e12,
+                        "frac_bf16_peak": flops / t / 1e12 / PEAK_BF16_TFLOPS,
+                        "flops": flops, "flops_dense": wl.attn_flops_dense()}
+    for name, nbytes in (("pack", pack_bytes), ("unpack", pack_bytes), ("merge", merge_bytes),
+                         ("exchange_in", pack_bytes), ("exchange_out", merge_bytes),
+                         ("send", merge_bytes)):
+        if name in kms:
+            t = kms[name] * 1e-3
+            kern[name] = {"us": kms[name] * 1e3, "GBps_warm": nbytes / t / 1e9,
+                          "frac_hbm_peak": nbytes / t / 1e9 / PEAK_HBM_GBPS, "bytes": nbytes}
+    if wl.B == 1 and "send" in kern:
+        kern["send"]["note"] = "identity layout for B=1: no kernel"
+
+    value = flops / (ms_per_step * 1e-3) / 1e12 if args.only in (None, "attn") else None
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "S_global": wl.S, "H": wl.H, "D": wl.D,
+                   "W": wl.W, "A": wl.A, "S_local": wl.S_local,
+                   "attn_q": [wl.B, wl.attn_rows, wl.attn_heads, wl.D],
+                   "attn_kv": [wl.B, wl.S, wl.attn_heads, wl.D], "masked": wl.masked,
+                   "parallelism": "one rank's share, exchange simulated on one GPU"},
+    }
+    if "attn" in kern:
+        out["roofline"] = {"bound": "mfma", "achieved": kern["attn"]["TFLOPs"],
+                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": kern["attn"]["TFLOPs"] / PEAK_BF16_TFLOPS, "traffic": None,
+                           "kernel": "attn_fwd_kernel"}
+    out["kernels"] = kern
+    if args.only is None and not args.no_cold:
+        pc, uc = cold_layout_gbps(wl, dev)
+        out["layout_cold"] = {"pack_GBps": pc, "unpack_GBps": uc,
+                              "pack_frac_hbm_peak": pc / PEAK_HBM_GBPS,
+                              "unpack_frac_hbm_peak": uc / PEAK_HBM_GBPS,
+                              "note": "rotating buffer sets > 512 MB (misses the 256 MB MALL)"}
+    if args.only is None:
+        out["parity"] = parity_sample(path, wl)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(wl, path.full, path.mask_np, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,24 @@
+"""MI355X-native hot path of context-parallel diffusion attention (one GPU's share).
+
+The compute lives in ``libcpattn.so`` (HIP, gfx950), whose C ABI is declared in
+``include/cp_attn.h``; this package is its thin Python binding.  Importing the
+package does not load the library; the first call does, and raises if it is not
+built.
+"""
+
+from ._lib import CpError, load  # noqa: F401
+from .ops import (  # noqa: F401
+    clear_staging,
+    cp_attn_localq_globalkv,
+    cp_output_reverse,
+    cp_pack_qkv_dst_major,
+    cp_sim_exchange,
+    cp_unpack_head_sharded,
+    staging_buffer,
+)
+
+__all__ = [
+    "CpError", "load", "staging_buffer", "clear_staging",
+    "cp_pack_qkv_dst_major", "cp_sim_exchange", "cp_unpack_head_sharded",
+    "cp_attn_localq_globalkv", "cp_output_reverse",
+]

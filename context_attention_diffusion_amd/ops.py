@@ -1,0 +1,183 @@
+"""Torch-facing wrappers of the libcpattn C ABI (argument marshalling only).
+
+Each function checks that tensors are on a GPU, contiguous and of the right
+dtype, allocates outputs the caller did not supply, and calls the entry point of
+the same name on the current HIP stream.  Every step of the computation runs in
+the library's kernels; nothing here computes on tensor data.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.bfloat16: _lib.CP_DTYPE_BF16, torch.float16: _lib.CP_DTYPE_FP16}
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"dtype {t.dtype} not supported; use bfloat16 or float16") from None
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# ---------------------------------------------------------------- staging cache
+
+_STAGING: dict[tuple, torch.Tensor] = {}
+
+
+def staging_buffer(role: str, shape, dtype, device) -> torch.Tensor:
+    """Reusable staging buffer keyed by (role, shape, dtype, device index).
+
+    Same contract as the staging cache of the sglang PR #33667 summary
+    (implementation breakdown item 1): a role's buffer is fully consumed, in
+    stream order, before the next call with that role overwrites it, so reuse is
+    safe on one stream; use from several streams needs explicit events.  During
+    stream capture a fresh buffer is returned instead, so that a graph never
+    shares memory with eager calls.
+    """
+    device = torch.device(device)
+    shape = tuple(int(s) for s in shape)
+    if torch.cuda.is_current_stream_capturing():
+        return torch.empty(shape, dtype=dtype, device=device)
+    key = (role, shape, dtype, device.index)
+    buf = _STAGING.get(key)
+    if buf is None:
+        buf = torch.empty(shape, dtype=dtype, device=device)
+        _STAGING[key] = buf
+    return buf
+
+
+def clear_staging() -> None:
+    _STAGING.clear()
+
+
+# ---------------------------------------------------------------- entry points
+
+def cp_pack_qkv_dst_major(q, k, v, W: int, staging=None, stream=None) -> torch.Tensor:
+    """[B,S_l,H,D] x3 -> staging [W, B*S_l, H/W, 3D] (destination-major, last axis q|k|v)."""
+    lib = _lib.load()
+    B, Sl, H, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    if H % W:
+        raise ValueError("H must divide by W")
+    shape = (W, B * Sl, H // W, 3 * D)
+    if staging is None:
+        staging = staging_buffer("cp_pack_send", shape, q.dtype, q.device)
+    if tuple(staging.shape) != shape or staging.dtype != q.dtype:
+        raise ValueError(f"staging must be {shape} {q.dtype}")
+    _lib.check("cp_pack_qkv_dst_major", lib.cp_pack_qkv_dst_major(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(staging, "staging"),
+        B, Sl, H, D, W, _dtype_code(q), _stream(stream)))
+    return staging
+
+
+def cp_sim_exchange(sends, rank: int, recv=None, stream=None) -> torch.Tensor:
+    """Single-GPU stand-in for the all-to-all: ``recv`` chunk r = chunk ``rank`` of ``sends[r]``."""
+    lib = _lib.load()
+    W = len(sends)
+    nbytes = sends[0].numel() * sends[0].element_size()
+    for s in sends:
+        if s.shape != sends[0].shape or s.dtype != sends[0].dtype:
+            raise ValueError("send buffers must share shape and dtype")
+    if recv is None:
+        recv = torch.empty_like(sends[0])
+    if recv.numel() * recv.element_size() != nbytes:
+        raise ValueError("recv must have the size of one send buffer")
+    arr = (ctypes.c_void_p * W)(*[_dev(s, f"sends[{i}]") for i, s in enumerate(sends)])
+    _lib.check("cp_sim_exchange", lib.cp_sim_exchange(
+        arr, _dev(recv, "recv"), W, rank, nbytes, _stream(stream)))
+    return recv
+
+
+def cp_unpack_head_sharded(recv, B: int, W: int, out=None, stream=None):
+    """recv [W, B*S_l, H_l, 3D] -> (q, k, v), each [B, W*S_l, H_l, D]."""
+    lib = _lib.load()
+    W_, rows, Hl, D3 = recv.shape
+    if W_ != W or rows % B or D3 % 3:
+        raise ValueError("recv shape does not match W / B")
+    Sl, D = rows // B, D3 // 3
+    shape = (B, W * Sl, Hl, D)
+    if out is None:
+        out = tuple(torch.empty(shape, dtype=recv.dtype, device=recv.device) for _ in range(3))
+    for t in out:
+        if tuple(t.shape) != shape or t.dtype != recv.dtype:
+            raise ValueError(f"outputs must be {shape} {recv.dtype}")
+    _lib.check("cp_unpack_head_sharded", lib.cp_unpack_head_sharded(
+        _dev(recv, "recv"), _dev(out[0], "q_out"), _dev(out[1], "k_out"), _dev(out[2], "v_out"),
+        B, Sl, Hl, D, W, _dtype_code(recv), _stream(stream)))
+    return out
+
+
+def cp_attn_localq_globalkv(q, k, v, key_mask=None, scale=None, out=None, causal=False,
+                            stream=None) -> torch.Tensor:
+    """Non-causal attention: q [B,Sq,H,D] vs k, v [B,Skv,H,D] (bf16), optional uint8 mask [B,Skv]."""
+    lib = _lib.load()
+    B, Sq, H, D = q.shape
+    Skv = k.shape[1]
+    if k.shape != (B, Skv, H, D) or v.shape != k.shape:
+        raise ValueError("k, v must be [B, Skv, H, D] matching q")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("attention takes bfloat16 q, k, v")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    mask_ptr = None
+    if key_mask is not None:
+        if key_mask.dtype not in (torch.uint8, torch.bool) or tuple(key_mask.shape) != (B, Skv):
+            raise ValueError("key_mask must be uint8/bool [B, Skv]")
+        mask_ptr = _dev(key_mask, "key_mask")
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    _lib.check("cp_attn_localq_globalkv", lib.cp_attn_localq_globalkv(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), mask_ptr, _dev(out, "o"),
+        B, Sq, Skv, H, D, float(scale), int(bool(causal)), _stream(stream)))
+    return out
+
+
+def cp_output_reverse(phase: int, src, W: int, B: int, out=None, stream=None) -> torch.Tensor:
+    """phase 0: [B, W*S_l, H_l, D] -> [W, B, S_l, H_l, D]; phase 1: [W,B,S_l,H_l,D] -> [B,S_l,W*H_l,D]."""
+    lib = _lib.load()
+    if phase == 0:
+        B_, S, Hl, D = src.shape
+        if B_ != B or S % W:
+            raise ValueError("src must be [B, W*S_l, H_l, D]")
+        Sl = S // W
+        shape = (W, B, Sl, Hl, D)
+    elif phase == 1:
+        W_, B_, Sl, Hl, D = src.shape
+        if W_ != W or B_ != B:
+            raise ValueError("src must be [W, B, S_l, H_l, D]")
+        shape = (B, Sl, W * Hl, D)
+    else:
+        raise ValueError("phase must be 0 (send) or 1 (merge)")
+    if out is None:
+        out = torch.empty(shape, dtype=src.dtype, device=src.device)
+    if tuple(out.shape) != shape or out.dtype != src.dtype:
+        raise ValueError(f"out must be {shape} {src.dtype}")
+    _lib.check("cp_output_reverse", lib.cp_output_reverse(
+        phase, _dev(src, "src"), _dev(out, "dst"), B, Sl, Hl, D, W, _dtype_code(src),
+        _stream(stream)))
+    return out

@@ -1,0 +1,180 @@
+/*
+ * cp_attn.h -- C ABI of libcpattn.so: one GPU's share of context-parallel
+ * diffusion-transformer attention on AMD MI355X (gfx950).
+ *
+ * The library covers the per-rank hot path of Ulysses / AllGather-KV context
+ * parallelism:
+ *   1. cp_pack_qkv_dst_major   -- Ulysses input exchange, send side
+ *   2. cp_sim_exchange         -- the W-way chunk exchange, simulated on one GPU
+ *   3. cp_unpack_head_sharded  -- Ulysses input exchange, receive side
+ *   4. cp_attn_localq_globalkv -- non-causal local-Q / global-KV attention
+ *   5. cp_output_reverse       -- Ulysses output exchange (send layout, merge)
+ *
+ * Sources, by page and section:
+ *   [sglang#33667]   prhub summary of sglang PR #33667 (pack the Ulysses QKV
+ *                    all-to-all into one collective and reuse staging buffers):
+ *                    "Implementation breakdown", "Key source snippets".
+ *   [vllm-omni#7641] vllm-omni PR #7641, "[Feature] Compose Ulysses with
+ *                    AllGather-KV as a 2D diffusion SP": commit message and
+ *                    review-fix commits.
+ *   [chitu-fastcp]   ChituDiffusion docs, "Install and enable Fast CP":
+ *                    "Support scope".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every pointer argument is DEVICE memory allocated and owned by the
+ * caller; the library never allocates, frees or retains a pointer past the call.
+ * Tensors are dense, row-major ("contiguous BSHD") and must start on a 16-byte
+ * boundary.  Outputs are fully overwritten; nothing stale is read from them.
+ *
+ * Streams.  `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ * call only enqueues work on that stream and returns; results are visible to
+ * later work on the same stream.  A staging buffer reused across calls is safe
+ * under in-order use on one stream (or with explicit events); using one buffer
+ * from two streams without synchronisation is a data race.  The library keeps
+ * no state and may be called from several host threads at once.
+ *
+ * Errors.  Every entry point returns 0 (CP_OK) or a CP_ERR_* code.  All argument
+ * checks run on the host before anything is enqueued, so a rejected call writes
+ * nothing.  There is no fallback path: an unsupported request fails.  A fault
+ * inside a kernel surfaces at the caller's next synchronisation.  The message for
+ * a code comes from cp_status_string().
+ *
+ * Dtypes.  The layout entry points move 2-byte elements bit-exactly and accept
+ * CP_DTYPE_BF16 and CP_DTYPE_FP16 (the packed path of [sglang#33667] is limited
+ * to those).  Attention is bf16 only.
+ */
+#ifndef CP_ATTN_H
+#define CP_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CP_ABI_VERSION 1
+
+typedef struct ihipStream_t* cp_stream_t; /* == hipStream_t */
+
+enum cp_status {
+  CP_OK = 0,
+  CP_ERR_NULL = 1,         /* a required pointer is NULL */
+  CP_ERR_DTYPE = 2,        /* dtype code not supported by this entry point */
+  CP_ERR_SHAPE = 3,        /* a size is < 1, or the problem exceeds the supported extent */
+  CP_ERR_DIVISIBILITY = 4, /* H % W != 0, or a chunk does not divide evenly */
+  CP_ERR_HEAD_DIM = 5,     /* D not supported (layout: D % 8 != 0; attention: D not 64/128) */
+  CP_ERR_ALIGNMENT = 6,    /* a pointer is not 16-byte aligned */
+  CP_ERR_ALIAS = 7,        /* an output overlaps an input or another output */
+  CP_ERR_SCALE = 8,        /* softmax scale is not finite or not > 0 */
+  CP_ERR_UNSUPPORTED = 9,  /* a valid but unsupported request (causal, bad phase, W too large) */
+  CP_ERR_HIP = 10          /* the HIP runtime rejected the launch */
+};
+
+enum cp_dtype { CP_DTYPE_BF16 = 0, CP_DTYPE_FP16 = 1 };
+
+/* Version of this ABI (CP_ABI_VERSION). */
+int cp_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* cp_status_string(int status);
+
+/*
+ * Ulysses input exchange, send side: destination-major pack of Q, K and V into
+ * one staging buffer, so that a single all-to-all moves all three tensors
+ * ([sglang#33667], implementation breakdown items 2-3 and the usp.py excerpt of
+ * _usp_input_all_to_all_qkv).
+ *
+ *   q, k, v : [B][S_local][H][D]            (this rank's sequence shard, all heads)
+ *   staging : [W][B*S_local][H/W][3*D]      (chunk j goes to rank j)
+ *   staging[j][b*S_local+s][hl][c*D+d] = X_c[b][s][j*(H/W)+hl][d],  X_0..2 = q, k, v
+ *
+ * Requires B, S_local, H, W >= 1, H % W == 0, D % 8 == 0 (rows of whole 16-byte
+ * vectors), all four pointers 16-byte aligned, staging disjoint from q, k, v.
+ */
+int cp_pack_qkv_dst_major(const void* q, const void* k, const void* v, void* staging,
+                          int64_t B, int64_t S_local, int64_t H, int64_t D, int64_t W,
+                          int dtype, cp_stream_t stream);
+
+/*
+ * Simulated W-way all-to-all, receive side of one rank (the single-GPU stand-in
+ * for the collective in [sglang#33667]'s unit-test excerpt): the chunk `rank`
+ * of every sender's buffer becomes chunk r of this rank's receive buffer,
+ *
+ *   recv[r*C .. (r+1)*C) = sends[r][rank*C .. (rank+1)*C),  C = bytes_per_rank / W.
+ *
+ *   sends : host array of W device pointers, each to bytes_per_rank bytes
+ *   recv  : device buffer of bytes_per_rank bytes
+ *
+ * Requires 1 <= W <= 64, 0 <= rank < W, bytes_per_rank % (16*W) == 0, every
+ * pointer 16-byte aligned, recv disjoint from every send buffer.
+ */
+int cp_sim_exchange(const void* const* sends, void* recv, int64_t W, int64_t rank,
+                    int64_t bytes_per_rank, cp_stream_t stream);
+
+/*
+ * Ulysses input exchange, receive side: split the received staging buffer into
+ * head-sharded Q, K, V with the source-rank axis placed in front of the
+ * sequence axis ([sglang#33667], usp.py excerpt: a view for B == 1, a
+ * rank/batch permute for B > 1, then a split of the last axis by D).
+ *
+ *   recv             : [W][B*S_local][H_local][3*D]
+ *   q_out/k_out/v_out: [B][W*S_local][H_local][D]
+ *   X_c[b][r*S_local+s][hl][d] = recv[r][b*S_local+s][hl][c*D+d]
+ *
+ * Requires sizes >= 1, D % 8 == 0, 16-byte aligned pointers, the three outputs
+ * pairwise disjoint and disjoint from recv.
+ */
+int cp_unpack_head_sharded(const void* recv, void* q_out, void* k_out, void* v_out,
+                           int64_t B, int64_t S_local, int64_t H_local, int64_t D,
+                           int64_t W, int dtype, cp_stream_t stream);
+
+/*
+ * Non-causal multi-head attention of local queries against global keys, the
+ * plain problem an AllGather-KV rank hands to its backend ([vllm-omni#7641],
+ * commit message; MHA, BF16, D 128 in [chitu-fastcp] "Support scope"):
+ *
+ *   o[b,i,h,:] = sum_{j valid} softmax_j(scale * q[b,i,h,:] . k[b,j,h,:]) v[b,j,h,:]
+ *
+ *   q, o     : [B][Sq][H][D]  bf16
+ *   k, v     : [B][Skv][H][D] bf16
+ *   key_mask : NULL, or [B][Skv] uint8 key-validity mask, nonzero = attend (the
+ *              2D key mask of [vllm-omni#7641]'s review fixes; any alignment)
+ *   scale    : softmax scale, finite and > 0 (1/sqrt(D) for standard attention)
+ *   causal   : must be 0 (causal attention is rejected, as in [vllm-omni#7641])
+ *
+ * Softmax statistics and accumulation are fp32; probabilities are rounded to
+ * bf16 before the P.V product; o is rounded to nearest-even bf16.  A query row
+ * whose batch has no valid key gets zeros.  Requires B, Sq, Skv, H >= 1,
+ * D in {64, 128}, q/k/v/o 16-byte aligned, o disjoint from q, k, v.
+ */
+int cp_attn_localq_globalkv(const void* q, const void* k, const void* v,
+                            const uint8_t* key_mask, void* o,
+                            int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D,
+                            float scale, int causal, cp_stream_t stream);
+
+/*
+ * Ulysses output exchange ([sglang#33667] names _usp_output_all_to_all in its
+ * implementation breakdown; [vllm-omni#7641] ends each attention with the
+ * reverse Ulysses step).  Read as the exact inverse of the input exchange with
+ * the same flat-chunk collective, it has a send phase and a merge phase:
+ *
+ *   phase 0 (SEND) : src [B][W*S_local][H_local][D] -> dst [W][B][S_local][H_local][D]
+ *                    dst[r][b][s][hl][d] = src[b][r*S_local+s][hl][d]
+ *                    (the identity on memory when B == 1)
+ *   phase 1 (MERGE): src [W][B][S_local][H_local][D] -> dst [B][S_local][W*H_local][D]
+ *                    dst[b][s][j*H_local+hl][d] = src[j][b][s][hl][d]
+ *
+ * Requires sizes >= 1, D % 8 == 0, 16-byte aligned pointers, dst disjoint from
+ * src, phase in {0, 1}.
+ */
+int cp_output_reverse(int phase, const void* src, void* dst,
+                      int64_t B, int64_t S_local, int64_t H_local, int64_t D, int64_t W,
+                      int dtype, cp_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CP_ATTN_H */

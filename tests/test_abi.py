@@ -1,0 +1,190 @@
+"""The C-ABI library loads, exports every symbol include/cp_attn.h declares, and
+rejects invalid arguments on the host before enqueuing anything (CPU only).
+
+The error-path calls pass fake, never-dereferenced addresses; every one of them
+must be rejected by host validation.  They are skipped on a machine with a GPU
+so that a validation bug can never turn them into a real launch.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from context_attention_diffusion_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cp_attn.h")
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    syms = _declared_symbols()
+    for name in ("cp_pack_qkv_dst_major", "cp_unpack_head_sharded", "cp_attn_localq_globalkv",
+                 "cp_output_reverse", "cp_sim_exchange", "cp_status_string", "cp_abi_version"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    syms = _declared_symbols()
+    assert set(syms) == set(_lib.SIGNATURES)
+    for name in syms:
+        assert hasattr(lib, name), name
+    assert lib.cp_abi_version() == _lib.ABI_VERSION
+
+
+def test_status_strings():
+    lib = _lib.load()
+    seen = set()
+    for code in range(0, 11):
+        s = lib.cp_status_string(code).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.cp_status_string(99).decode() == "unknown status code"
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+cpu_only = pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation tests run only without a GPU")
+
+A = 0x10000          # fake 16-byte aligned addresses, never dereferenced
+BIG = 1 << 40        # far apart so that nothing overlaps unless intended
+BF16 = _lib.CP_DTYPE_BF16
+
+
+def _pack(**kw):
+    a = dict(q=A, k=A + BIG, v=A + 2 * BIG, st=A + 3 * BIG, B=1, Sl=4, H=4, D=128, W=2,
+             dtype=BF16)
+    a.update(kw)
+    return _lib.load().cp_pack_qkv_dst_major(a["q"], a["k"], a["v"], a["st"], a["B"], a["Sl"],
+                                             a["H"], a["D"], a["W"], a["dtype"], None)
+
+
+def _unpack(**kw):
+    a = dict(r=A, q=A + BIG, k=A + 2 * BIG, v=A + 3 * BIG, B=1, Sl=4, Hl=2, D=128, W=2,
+             dtype=BF16)
+    a.update(kw)
+    return _lib.load().cp_unpack_head_sharded(a["r"], a["q"], a["k"], a["v"], a["B"], a["Sl"],
+                                              a["Hl"], a["D"], a["W"], a["dtype"], None)
+
+
+def _attn(**kw):
+    a = dict(q=A, k=A + BIG, v=A + 2 * BIG, m=None, o=A + 3 * BIG, B=1, Sq=8, Skv=16, H=2,
+             D=128, scale=0.125, causal=0)
+    a.update(kw)
+    return _lib.load().cp_attn_localq_globalkv(a["q"], a["k"], a["v"], a["m"], a["o"], a["B"],
+                                               a["Sq"], a["Skv"], a["H"], a["D"], a["scale"],
+                                               a["causal"], None)
+
+
+def _rev(**kw):
+    a = dict(phase=0, s=A, d=A + BIG, B=1, Sl=4, Hl=2, D=128, W=2, dtype=BF16)
+    a.update(kw)
+    return _lib.load().cp_output_reverse(a["phase"], a["s"], a["d"], a["B"], a["Sl"], a["Hl"],
+                                         a["D"], a["W"], a["dtype"], None)
+
+
+def _xchg(W=2, rank=0, nbytes=4096, sends=None, recv=A + 8 * BIG):
+    if sends is None:
+        sends = [A + i * BIG for i in range(W)]
+    arr = (ctypes.c_void_p * len(sends))(*sends)
+    return _lib.load().cp_sim_exchange(arr, recv, W, rank, nbytes, None)
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.CP_ERR_NULL),
+    (dict(st=None), _lib.CP_ERR_NULL),
+    (dict(dtype=7), _lib.CP_ERR_DTYPE),
+    (dict(B=0), _lib.CP_ERR_SHAPE),
+    (dict(Sl=-1), _lib.CP_ERR_SHAPE),
+    (dict(W=0), _lib.CP_ERR_SHAPE),
+    (dict(H=6, W=4), _lib.CP_ERR_DIVISIBILITY),
+    (dict(D=12), _lib.CP_ERR_HEAD_DIM),
+    (dict(D=0), _lib.CP_ERR_HEAD_DIM),
+    (dict(q=A + 8), _lib.CP_ERR_ALIGNMENT),
+    (dict(st=A + 3 * BIG + 2), _lib.CP_ERR_ALIGNMENT),
+    (dict(st=A + 64), _lib.CP_ERR_ALIAS),
+    (dict(B=1 << 20, Sl=1 << 20, H=64), _lib.CP_ERR_SHAPE),
+])
+def test_pack_rejects(kw, code):
+    assert _pack(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(v=None), _lib.CP_ERR_NULL),
+    (dict(dtype=-1), _lib.CP_ERR_DTYPE),
+    (dict(Hl=0), _lib.CP_ERR_SHAPE),
+    (dict(D=20), _lib.CP_ERR_HEAD_DIM),
+    (dict(k=A + 2 * BIG + 4), _lib.CP_ERR_ALIGNMENT),
+    (dict(k=A + BIG + 16), _lib.CP_ERR_ALIAS),       # k_out overlaps q_out
+    (dict(q=A + 32), _lib.CP_ERR_ALIAS),             # q_out overlaps recv
+    (dict(B=1 << 16, Sl=1 << 16, W=8), _lib.CP_ERR_SHAPE),
+])
+def test_unpack_rejects(kw, code):
+    assert _unpack(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=None), _lib.CP_ERR_NULL),
+    (dict(Sq=0), _lib.CP_ERR_SHAPE),
+    (dict(Skv=0), _lib.CP_ERR_SHAPE),
+    (dict(H=0), _lib.CP_ERR_SHAPE),
+    (dict(D=96), _lib.CP_ERR_HEAD_DIM),
+    (dict(D=256), _lib.CP_ERR_HEAD_DIM),
+    (dict(scale=0.0), _lib.CP_ERR_SCALE),
+    (dict(scale=-1.0), _lib.CP_ERR_SCALE),
+    (dict(scale=math.nan), _lib.CP_ERR_SCALE),
+    (dict(scale=math.inf), _lib.CP_ERR_SCALE),
+    (dict(causal=1), _lib.CP_ERR_UNSUPPORTED),
+    (dict(v=A + 2 * BIG + 8), _lib.CP_ERR_ALIGNMENT),
+    (dict(o=A + 16), _lib.CP_ERR_ALIAS),             # o overlaps q
+    (dict(o=A + BIG + 16), _lib.CP_ERR_ALIAS),       # o overlaps k
+    (dict(m=A + 3 * BIG + 16), _lib.CP_ERR_ALIAS),   # mask inside o
+    (dict(B=1 << 31), _lib.CP_ERR_SHAPE),
+])
+def test_attention_rejects(kw, code):
+    assert _attn(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(s=None), _lib.CP_ERR_NULL),
+    (dict(phase=2), _lib.CP_ERR_UNSUPPORTED),
+    (dict(phase=-1), _lib.CP_ERR_UNSUPPORTED),
+    (dict(dtype=3), _lib.CP_ERR_DTYPE),
+    (dict(W=0), _lib.CP_ERR_SHAPE),
+    (dict(D=4), _lib.CP_ERR_HEAD_DIM),
+    (dict(d=A + BIG + 8), _lib.CP_ERR_ALIGNMENT),
+    (dict(d=A + 128), _lib.CP_ERR_ALIAS),
+])
+def test_reverse_rejects(kw, code):
+    assert _rev(**kw) == code
+
+
+@cpu_only
+def test_exchange_rejects():
+    assert _xchg(W=0) == _lib.CP_ERR_SHAPE
+    assert _xchg(W=65, sends=[A + i * BIG for i in range(65)]) == _lib.CP_ERR_UNSUPPORTED
+    assert _xchg(rank=2) == _lib.CP_ERR_SHAPE
+    assert _xchg(rank=-1) == _lib.CP_ERR_SHAPE
+    assert _xchg(nbytes=48) == _lib.CP_ERR_DIVISIBILITY      # 48 % (16*2) != 0
+    assert _xchg(nbytes=0) == _lib.CP_ERR_SHAPE
+    assert _xchg(recv=A + 8 * BIG + 4) == _lib.CP_ERR_ALIGNMENT
+    assert _xchg(sends=[A, None]) == _lib.CP_ERR_NULL
+    assert _xchg(sends=[A, A + BIG + 8]) == _lib.CP_ERR_ALIGNMENT
+    assert _xchg(recv=A + 1024) == _lib.CP_ERR_ALIAS
+    assert _lib.load().cp_sim_exchange(None, A, 2, 0, 4096, None) == _lib.CP_ERR_NULL

@@ -1,0 +1,172 @@
+"""GPU parity of cp_attn_localq_globalkv against the fp64 oracle.
+
+Bar: max|err| <= 2e-2 and mean|err| <= 2e-3 against the fp64 oracle on the same
+bf16 inputs.  Small and ragged shapes are compared element by element over the
+whole output; the full-size workloads are compared on sampled output rows that
+the oracle computes one by one, plus properties that hold at any size.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import attention as OA
+from oracle import bf16
+
+pytestmark = pytest.mark.gpu
+
+MAX_ERR = 2e-2
+MEAN_ERR = 2e-3
+
+
+@pytest.fixture(scope="module")
+def gu():
+    import gpu_util
+    return gpu_util
+
+
+def _run(gu, q, k, v, mask=None, scale=None):
+    import context_attention_diffusion_amd as cp
+    qd, kd, vd = gu.to_dev(q), gu.to_dev(k), gu.to_dev(v)
+    md = None if mask is None else torch.from_numpy(mask).to(gu.DEV)
+    o = cp.cp_attn_localq_globalkv(qd, kd, vd, md, scale=scale)
+    torch.cuda.synchronize()
+    return gu.to_f64(o)
+
+
+def _assert_close(got, ref, what):
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    mx, mean = float(err.max()), float(err.mean())
+    print(f"  {what}: max|err| {mx:.3e} mean|err| {mean:.3e}", flush=True)
+    assert mx <= MAX_ERR and mean <= MEAN_ERR, f"{what}: max {mx} mean {mean}"
+
+
+def _rand_bits(shape, seed, mult=1.0):
+    x = np.random.default_rng(seed).standard_normal(shape) * mult
+    return bf16.f64_to_bits_rne(x)
+
+
+def test_tiny_workload_full_compare(gu):
+    wl = workloads.WORKLOADS["tiny_w2"]
+    q, k, v = workloads.global_qkv(wl)
+    q = np.ascontiguousarray(q[:, :wl.attn_rows])
+    got = _run(gu, q, k, v, scale=1.0 / math.sqrt(wl.D))
+    ref = OA.attention(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v),
+                       scale=1.0 / math.sqrt(wl.D))
+    _assert_close(got, ref, "tiny_w2")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Sq,Skv", [(1, 1), (7, 5), (127, 63), (129, 65), (300, 200), (33, 513)])
+@pytest.mark.parametrize("masked", [False, True])
+def test_ragged_shapes(gu, D, Sq, Skv, masked):
+    B, H = 2, 3
+    seed = Sq * 7919 + Skv * 31 + D + int(masked)
+    q = _rand_bits((B, Sq, H, D), seed)
+    k = _rand_bits((B, Skv, H, D), seed + 1)
+    v = _rand_bits((B, Skv, H, D), seed + 2)
+    mask = None
+    if masked:
+        mask = (np.random.default_rng(seed + 3).random((B, Skv)) > 0.35).astype(np.uint8)
+        mask[:, 0] = 1
+    print(f"[attn] ragged D={D} Sq={Sq} Skv={Skv} masked={masked}", flush=True)
+    got = _run(gu, q, k, v, mask)
+    ref = OA.attention(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), mask)
+    _assert_close(got, ref, f"D{D} Sq{Sq} Skv{Skv} m{int(masked)}")
+
+
+def test_scale_and_large_logits(gu):
+    B, Sq, Skv, H, D = 1, 130, 300, 2, 128
+    q = _rand_bits((B, Sq, H, D), 41, mult=4.0)
+    k = _rand_bits((B, Skv, H, D), 42, mult=4.0)
+    v = _rand_bits((B, Skv, H, D), 43)
+    for scale in (0.3, 1.0 / math.sqrt(D), 0.01):
+        got = _run(gu, q, k, v, scale=scale)
+        ref = OA.attention(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), scale=scale)
+        _assert_close(got, ref, f"scale {scale}")
+
+
+def test_mask_closed_forms(gu):
+    B, Sq, Skv, H, D = 3, 70, 150, 2, 128
+    q = _rand_bits((B, Sq, H, D), 51)
+    k = _rand_bits((B, Skv, H, D), 52)
+    v = _rand_bits((B, Skv, H, D), 53)
+    mask = np.zeros((B, Skv), np.uint8)
+    mask[0, 77] = 1            # one valid key: every output row is that value row
+    mask[2, :] = 1
+    mask[2, 100:] = 0          # batch 1 stays fully masked: zeros
+    got = _run(gu, q, k, v, mask)
+    vf = bf16.bits_to_f64(v)
+    for i in range(Sq):
+        np.testing.assert_array_equal(got[0, i], vf[0, 77])
+    assert (got[1] == 0).all()
+    ref = OA.attention(bf16.bits_to_f64(q), bf16.bits_to_f64(k), vf, mask)
+    _assert_close(got[2], ref[2], "partial mask")
+
+
+def test_zero_query_gives_mean_of_valid_values(gu):
+    B, Sq, Skv, H, D = 2, 40, 333, 2, 64
+    q = np.zeros((B, Sq, H, D), np.uint16)
+    k = _rand_bits((B, Skv, H, D), 61)
+    v = _rand_bits((B, Skv, H, D), 62)
+    mask = (np.random.default_rng(63).random((B, Skv)) > 0.5).astype(np.uint8)
+    got = _run(gu, q, k, v, mask)
+    vf = bf16.bits_to_f64(v)
+    for b in range(B):
+        mean = vf[b][mask[b] != 0].mean(axis=0)
+        _assert_close(got[b], np.broadcast_to(mean, got[b].shape), f"Q=0 batch {b}")
+
+
+def test_key_permutation_invariance(gu):
+    B, Sq, Skv, H, D = 1, 128, 256, 2, 128
+    q = _rand_bits((B, Sq, H, D), 71)
+    k = _rand_bits((B, Skv, H, D), 72)
+    v = _rand_bits((B, Skv, H, D), 73)
+    perm = np.random.default_rng(74).permutation(Skv)
+    a = _run(gu, q, k, v)
+    b = _run(gu, q, np.ascontiguousarray(k[:, perm]), np.ascontiguousarray(v[:, perm]))
+    _assert_close(a, b, "permuted keys")
+
+
+def test_deterministic(gu):
+    B, Sq, Skv, H, D = 1, 256, 700, 4, 128
+    q, k, v = (_rand_bits((B, s, H, D), 80 + i) for i, s in enumerate((Sq, Skv, Skv)))
+    a = _run(gu, q, k, v)
+    b = _run(gu, q, k, v)
+    np.testing.assert_array_equal(a, b)
+
+
+def _sample_rows(wl, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = {(0, 0, 0), (wl.B - 1, wl.attn_rows - 1, wl.attn_heads - 1),
+            (0, wl.attn_rows - 1, 0), (wl.B - 1, 0, wl.attn_heads - 1)}
+    while len(rows) < n:
+        rows.add((int(rng.integers(wl.B)), int(rng.integers(wl.attn_rows)),
+                  int(rng.integers(wl.attn_heads))))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["image_cp4", "image_cp8", "video_u2a2", "joint_cfg_cp4"])
+def test_full_size_workloads_sampled(gu, name):
+    wl = workloads.WORKLOADS[name]
+    print(f"[attn] full-size {name}", flush=True)
+    qg, kg, vg = workloads.global_qkv(wl, heads=wl.attn_heads)
+    q = np.ascontiguousarray(qg[:, :wl.attn_rows])
+    mask = workloads.key_mask(wl)
+    got = _run(gu, q, kg, vg, mask, scale=1.0 / math.sqrt(wl.D))
+    rows = _sample_rows(wl, 48, wl.seed)
+    ref = OA.attention_rows(bf16.bits_to_f64(q), bf16.bits_to_f64(kg), bf16.bits_to_f64(vg),
+                            rows, mask, scale=1.0 / math.sqrt(wl.D))
+    sel = np.stack([got[b, i, h] for (b, i, h) in rows])
+    _assert_close(sel, ref, f"{name} sampled rows")
+    # Any-size property: every output lies within [min, max] of the valid value rows.
+    vf = torch.from_numpy(vg).view(torch.int16).view(torch.bfloat16).float()
+    for b in range(wl.B):
+        valid = torch.ones(wl.S, dtype=torch.bool) if mask is None else torch.from_numpy(mask[b] != 0)
+        vv = vf[b][valid]
+        lo, hi = vv.min(dim=0).values.numpy(), vv.max(dim=0).values.numpy()
+        assert (got[b] >= lo - 1e-2).all() and (got[b] <= hi + 1e-2).all()

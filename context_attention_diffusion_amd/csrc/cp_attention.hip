@@ -12,15 +12,21 @@
 // LDS tiles, and every SIMD runs one wave of each group.  At the end the two
 // partial softmax states are merged through LDS.
 //
+//  * K and V tiles (64 keys) go from HBM straight into LDS with buffer loads
+//    that write LDS directly (no VGPR staging), row-major, with the 16-byte
+//    chunks of each row XOR-swizzled so that both readers below are free of
+//    bank conflicts.  Rows past the last key fall outside the buffer
+//    descriptor's range and arrive as zeros.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16.  With keys as the MFMA row
 //    dimension, each lane owns one query column and 16 key rows per 32x32
 //    block, so the row max and row sum are in-lane reductions plus one
-//    permlane32 swap.  Q stays in registers (the B operand) for the whole loop.
+//    exchange with lane ^ 32.  Q stays in registers (the B operand).
 //  * O^T = V^T P^T on the same MFMA.  The probabilities leave the S^T
-//    accumulators already in B-operand position; the 16 keys of each MFMA step
-//    are taken in the order the accumulator layout delivers them, and V is
-//    written to LDS transposed ([d][key]) in that same key order, so every
-//    operand is one 16-byte LDS read.
+//    accumulators already in B-operand position.  The V^T operand comes from
+//    the row-major V tile through ds_read_b64_tr_b16, which hands each lane
+//    four consecutive keys of one head-dim column; two such reads cover the
+//    eight keys a lane contributes to one MFMA step, in the order the
+//    accumulator layout delivers the matching probabilities.
 //  * Software pipeline per wave: iteration i issues the Q K^T MFMAs of its
 //    next tile while the VALU turns the current tile's scores into
 //    probabilities, then the P V MFMAs of the current tile while the VALU takes
@@ -49,7 +55,10 @@ namespace {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kGroupWaves = 4;
 constexpr int kGroups = 2;
@@ -59,41 +68,34 @@ constexpr int kNumXcd = 8;
 
 template <int D>
 struct Cfg {
-  static constexpr int BM = 32 * kGroupWaves;  // query rows per workgroup
-  static constexpr int BN = 64;                // keys per tile
-  static constexpr int KP = D + 8;             // K row pitch in LDS (elements); +16 B vs bank conflicts
-  static constexpr int VP = BN + 8;            // V^T row pitch in LDS (elements)
-  static constexpr int K_ELEMS = BN * KP;
-  static constexpr int V_ELEMS = D * VP;
-  static constexpr int VD = D / 8;             // 16-byte vectors per head row
-  static constexpr int LOADS = BN * VD / kGroupThreads;  // K (and V) vectors per thread per tile
-  static constexpr int KPT = LOADS;            // keys per thread in the V transpose
-  static constexpr int VGROUPS = BN / KPT;     // key groups per 16-byte column of V
-  static constexpr int DB = D / 32;            // 32-row blocks of O^T
-  static constexpr int KS = D / 16;            // 16-wide reduction steps of Q K^T
-  static constexpr int NCOMB = DB * 16 + 2;    // floats per lane in the group merge
-  static_assert(LOADS * kGroupThreads == BN * VD, "tile must split evenly");
-  static_assert(VGROUPS * VD == kGroupThreads, "V transpose mapping must cover the tile");
-  static_assert(KPT == 2 || KPT == 4, "V transpose writes 2 or 4 keys per store");
-  static_assert(kGroupWaves * 64 * NCOMB * 4 <= kGroups * 2 * K_ELEMS * 2,
-                "group merge must fit in the K buffers");
+  static constexpr int BM = 32 * kGroupWaves;   // query rows per workgroup
+  static constexpr int BN = 64;                 // keys per tile
+  static constexpr int RB = 2 * D;              // bytes per K/V row
+  static constexpr int TILE = BN * RB;          // bytes per K or V tile
+  static constexpr int SPT = TILE / 16 / kGroupThreads;  // 16-byte slots per thread per tile
+  static constexpr int CHUNKS = RB / 16;        // 16-byte chunks per row
+  static constexpr int RPL = 256 / RB;          // rows per 256-byte LDS line
+  static constexpr int DB = D / 32;             // 32-row blocks of O^T
+  static constexpr int KS = D / 16;             // 16-wide reduction steps of Q K^T
+  static constexpr int NCOMB = DB * 16 + 2;     // floats per lane in the group merge
+  // LDS bytes: K tiles [group][buf], V tiles [group][buf], bias rows [group][buf][BN]
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = kGroups * 2 * TILE;
+  static constexpr int BIAS_OFF = 2 * kGroups * 2 * TILE;
+  static constexpr int LDS_BYTES = BIAS_OFF + kGroups * 2 * BN * 4;
+  static_assert(SPT * kGroupThreads * 16 == TILE, "tile must split evenly into slots");
+  static_assert(kGroupWaves * 64 * NCOMB * 4 <= BIAS_OFF, "group merge must fit in the tiles");
+  // Chunk swizzle of a row (the 16-byte chunk index is XORed with it).  LDS
+  // serves 16 lanes of a 16-byte read, or 32 lanes of an 8-byte read, per pass
+  // over its 256 bytes of banks; the swizzle makes both passes conflict-free:
+  //  * K reads: 16 consecutive rows at one chunk -> 16 distinct 16-byte slots;
+  //  * V^T transpose reads: 4 consecutive rows x 4 consecutive chunks -> 16
+  //    distinct slots (bits 2-3 of the swizzle separate the 4 rows).
+  static __device__ __forceinline__ int swz(int key) {
+    return 4 * ((key / RPL) % (4 / RPL)) + (key / 4) % 4;
+  }
 };
 
-// Position of key offset `ko` (0..BN-1) inside a V^T row: bits 2 and 3 swapped,
-// which is the order in which a lane's accumulator rows enter one MFMA step.
-__device__ __forceinline__ int vt_pos(int ko) {
-  return (ko & ~12) | ((ko & 4) << 1) | ((ko & 8) >> 1);
-}
-
-// Two-element transposes of bf16 pairs: lo_pair(a, b) = {a.lo, b.lo}, hi_pair(a, b) = {a.hi, b.hi},
-// one v_perm_b32 each.
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-__device__ __forceinline__ uint32_t dword_of(const uint4& v, int w) {
-  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
-}
-
-// max / sum of x over lanes l and l ^ 32
 __device__ __forceinline__ float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
 
@@ -109,12 +111,13 @@ struct AttnArgs {
   float sc;     // scale * log2(e)
 };
 
+// The body is a device function behind a thin kernel: the LDS address-space
+// casts it needs are device-only, and keeping them out of the kernel itself lets
+// the host pass emit the kernel's launch stub.
 template <int D>
-__global__ void __launch_bounds__(kThreads) attn_fwd_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 kbuf[kGroups][2][C::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) __bf16 vbuf[kGroups][2][C::V_ELEMS];
-  __shared__ __attribute__((aligned(16))) float kbias[kGroups][2][C::BN];
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
   // ---- XCD-aware work numbering: consecutive logical tiles share an XCD.
   const int pid = blockIdx.x;
@@ -129,13 +132,13 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x;
   // Wave-uniform indices go through readfirstlane so that the compiler keeps
-  // them (and the buffer descriptors built from them) in scalar registers.
+  // them (and the buffer descriptors and LDS bases built from them) scalar.
   const int grp = __builtin_amdgcn_readfirstlane(tid / kGroupThreads);  // key-tile group
-  const int gt = tid % kGroupThreads;                                   // thread index inside the group
-  const int gw = __builtin_amdgcn_readfirstlane(gt >> 6);               // wave index inside the group
+  const int gt = tid % kGroupThreads;                                   // thread index in the group
+  const int gw = __builtin_amdgcn_readfirstlane(gt >> 6);               // wave index in the group
   const int lane = tid & 63;
   const int l32 = lane & 31;
-  const int hi = lane >> 5;                // which half of the wave: selects 8-wide k slices
+  const int hi = lane >> 5;  // half of the wave: selects the 8-wide k slice of an MFMA operand
 
   const size_t row_stride = size_t(a.H) * D;  // elements between consecutive sequence rows
   const __bf16* kbase = a.k + (size_t(b) * a.Skv * a.H + h) * D;
@@ -157,41 +160,40 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(AttnArgs a) {
   }
 
   const int n_tiles = (a.Skv + C::BN - 1) / C::BN;
-  const int n_iter = (n_tiles + 1) / 2;              // iterations of every wave
-  const int n_g = (n_tiles - grp + 1) / 2;           // tiles of this group
+  const int n_iter = (n_tiles + 1) / 2;     // iterations of every wave
+  const int n_g = (n_tiles - grp + 1) / 2;  // tiles of this group
   auto tile_of = [&](int i) { return 2 * i + grp; };
 
-  // ---- global -> register staging through buffer resources.  One descriptor
-  // per tile (base advanced to the tile's first key, scalar registers); fixed
-  // per-lane byte offsets; rows past the last key fall outside the descriptor's
-  // range and read as zero, so the loads need no bounds arithmetic.
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  uint4 kreg[C::LOADS], vreg[C::KPT];
-  float breg = 0.f;
-  const int vgrp = gt % C::VGROUPS;   // V: key group (KPT consecutive keys)
-  const int vcol = gt / C::VGROUPS;   // V: 16-byte column (8 head-dim values)
+  // ---- HBM -> LDS fill.  Slot s of a tile (16 bytes) holds chunk
+  // (s % CHUNKS) ^ swz(key) of row key = s / CHUNKS; instruction j of wave gw
+  // fills slots [(gw*SPT + j)*64, +64), lane-ordered.
   const uint32_t rs_bytes = uint32_t(row_stride) * 2u;
   const uint32_t valid_end = uint32_t(a.Skv - 1) * rs_bytes + uint32_t(D) * 2u;
-  uint32_t koff[C::LOADS], voff[C::KPT];
+  uint32_t goff[C::SPT];
 #pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int vec = gt + kGroupThreads * i;
-    koff[i] = uint32_t(vec / C::VD) * rs_bytes + uint32_t(vec % C::VD) * 16u;
+  for (int j = 0; j < C::SPT; ++j) {
+    const int slot = (gw * C::SPT + j) * 64 + lane;
+    const int key = slot / C::CHUNKS;
+    const int chunk = (slot % C::CHUNKS) ^ C::swz(key);
+    goff[j] = uint32_t(key) * rs_bytes + uint32_t(chunk) * 16u;
   }
-#pragma unroll
-  for (int i = 0; i < C::KPT; ++i) voff[i] = uint32_t(vgrp * C::KPT + i) * rs_bytes + uint32_t(vcol) * 16u;
-  auto tile_rsrc = [&](const __bf16* base, int t) {
+  auto fill = [&](const __bf16* base, int t, int lds_off) {
     const uint32_t off = uint32_t(t) * uint32_t(C::BN) * rs_bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(reinterpret_cast<const char*>(base)) + off, (short)0, int(valid_end - off),
         0x00020000);
-  };
-  auto as_uint4 = [](u32x4 x) { return uint4{x.x, x.y, x.z, x.w}; };
-
-  auto load_k = [&](int t) {
-    const auto rk = tile_rsrc(kbase, t);
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) kreg[i] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rk, koff[i], 0, 0));
+    for (int j = 0; j < C::SPT; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (lds_void*)(lds + lds_off + (gw * C::SPT + j) * 1024), 16, goff[j], 0, 0, 0);
+  };
+  auto k_off = [&](int buf) { return C::K_OFF + (grp * 2 + buf) * C::TILE; };
+  auto v_off = [&](int buf) { return C::V_OFF + (grp * 2 + buf) * C::TILE; };
+  float* bias_row = reinterpret_cast<float*>(lds + C::BIAS_OFF) + grp * 2 * C::BN;
+
+  // Key validity of tile t as an additive bias, one key per thread of wave 0.
+  float breg = 0.f;
+  auto bias_of = [&](int t) {
     if (gt < C::BN) {
       const int key = t * C::BN + gt;
       bool valid = key < a.Skv;
@@ -199,56 +201,35 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(AttnArgs a) {
       breg = valid ? 0.f : -INFINITY;
     }
   };
-  auto load_v = [&](int t) {
-    const auto rv = tile_rsrc(vbase, t);
-#pragma unroll
-    for (int i = 0; i < C::KPT; ++i) vreg[i] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rv, voff[i], 0, 0));
-  };
-  auto store_k = [&](int buf) {
-    __bf16* ks = kbuf[grp][buf];
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int vec = gt + kGroupThreads * i;
-      const int kr = vec / C::VD, kc = vec % C::VD;
-      *reinterpret_cast<uint4*>(ks + kr * C::KP + kc * 8) = kreg[i];
-    }
-    if (gt < C::BN) kbias[grp][buf][gt] = breg;
-  };
-  auto store_v = [&](int buf) {
-    __bf16* vs = vbuf[grp][buf];
-    const int pos = vt_pos(vgrp * C::KPT);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      __bf16* dst = vs + (vcol * 8 + e) * C::VP + pos;
-      if constexpr (C::KPT == 4) {
-        uint2 pr;
-        if (e & 1) {
-          pr.x = hi_pair(dword_of(vreg[0], w), dword_of(vreg[1], w));
-          pr.y = hi_pair(dword_of(vreg[2], w), dword_of(vreg[3], w));
-        } else {
-          pr.x = lo_pair(dword_of(vreg[0], w), dword_of(vreg[1], w));
-          pr.y = lo_pair(dword_of(vreg[2], w), dword_of(vreg[3], w));
-        }
-        *reinterpret_cast<uint2*>(dst) = pr;
-      } else {
-        const uint32_t x = (e & 1) ? hi_pair(dword_of(vreg[0], w), dword_of(vreg[1], w))
-                                   : lo_pair(dword_of(vreg[0], w), dword_of(vreg[1], w));
-        *reinterpret_cast<uint32_t*>(dst) = x;
-      }
-    }
+  auto store_bias = [&](int buf) {
+    if (gt < C::BN) bias_row[buf * C::BN + gt] = breg;
   };
 
-  // S^T[key][query] of one tile (two 32-key blocks) from K in LDS.
+  // ---- LDS readers
+  // K operand of S^T: row kb*32 + l32, chunk 2*kk + hi  ->  byte kb*32*RB + (kaddr ^ (kk * 32))
+  const int kswz = C::swz(l32);
+  const int kaddr = l32 * C::RB + ((hi ^ (kswz & 1)) * 16) + (kswz & ~1) * 16;
+  // V^T operand: lane (G = lane/16, i = lane%16) reads row 16m + 8r + 4hi + i/4, head-dim
+  // 32db + 16(G%2) + 4(i%4) .. +4  ->  byte (16m + 8r) * RB + (vaddr_r ^ (db * 64))
+  // (r = 0 / 1 for the first / second four keys of the step).
+  const int vG = lane >> 4, vi = lane & 15;
+  const int vrow = 4 * hi + vi / 4;
+  const int vj = 2 * (vG & 1) + ((vi & 3) >> 1);  // chunk within the 4-chunk group of this db
+  auto vaddr_of = [&](int r) {
+    const int f = C::swz(8 * r + vrow);
+    return vrow * C::RB + (vi & 1) * 8 + (vj ^ (f & 3)) * 16 + (f >> 2) * 64;
+  };
+  const int vaddr0 = vaddr_of(0), vaddr1 = vaddr_of(1);
+
+  // S^T[key][query] of one tile (two 32-key blocks).
   auto qk = [&](int buf, f32x16* s) {
-    const __bf16* ks = kbuf[grp][buf];
+    const char* kt = lds + k_off(buf);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < C::KS; ++kk) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * C::KP + kk * 16 + 8 * hi);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * C::RB + (kaddr ^ (kk * 32)));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc, 0, 0, 0);
       }
       s[kb] = acc;
@@ -258,11 +239,12 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(AttnArgs a) {
   // Accumulator row r of block kb is key kb*32 + 8*(r/4) + 4*hi + r%4.
   auto bias_max = [&](int buf, int t, f32x16* s) -> float {
     if (a.mask != nullptr || (t + 1) * C::BN > a.Skv) {
+      const float* br = bias_row + buf * C::BN;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float4 bb = *reinterpret_cast<const float4*>(&kbias[grp][buf][kb * 32 + 8 * g + 4 * hi]);
+          const float4 bb = *reinterpret_cast<const float4*>(br + kb * 32 + 8 * g + 4 * hi);
           s[kb][4 * g + 0] += bb.x;
           s[kb][4 * g + 1] += bb.y;
           s[kb][4 * g + 2] += bb.z;
@@ -287,8 +269,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(AttnArgs a) {
       for (int kk = 0; kk < 8; ++kk)
         pf[m][kk] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[m >> 1][8 * (m & 1) + kk], a.sc, -m_use));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-      {
+      for (int j = 0; j < 4; ++j) {
         const bf16x2 pr = {pf[m][2 * j], pf[m][2 * j + 1]};
         lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
       }
@@ -300,85 +281,113 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(AttnArgs a) {
   for (int db = 0; db < C::DB; ++db) acc_o[db] = f32x16{};
   // O^T[d][query] += V^T[d][keys] P^T[keys][query]
   auto pv = [&](int buf, const bf16x8* pf) {
-    const __bf16* vs = vbuf[grp][buf];
+    const char* vt = lds + v_off(buf);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * C::VP + 16 * m + 8 * hi);
+        const i16x4 lo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + 16 * m * C::RB + (vaddr0 ^ (db * 64))));
+        const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vt + (16 * m + 8) * C::RB + (vaddr1 ^ (db * 64))));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[m], acc_o[db], 0, 0, 0);
       }
   };
 
   float m_run = -INFINITY;  // running max, scaled log2 units (shared by lanes l, l^32)
   float l_run = 0.f;        // this lane's partial row sum
-  f32x16 s_cur[2], s_nxt[2];
+  f32x16 sc[2];             // scores of one tile
 
-  // ---- prologue: K of local tiles 0 and 1, V of tile 0, scores of tile 0
-  if (n_g > 0) {
-    load_k(tile_of(0));
-    store_k(0);
-    if (n_g > 1) {
-      load_k(tile_of(1));
-      store_k(1);
+  // Raise the running max to a tile max that exceeds it by more than 8.
+  auto rescale = [&](float mt_tile) {
+    const bool raise = mt_tile > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = raise ? mt_tile : m_run;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+      m_run = m_new;
     }
-    load_v(tile_of(0));
-    store_v(0);
-  }
-  __syncthreads();
-  if (n_g > 0) {
-    qk(0, s_cur);
-    m_run = bias_max(0, tile_of(0), s_cur);
-  }
-
-  // ---- main loop; every wave runs n_iter iterations so that barriers match
-  auto iteration = [&](int i, auto load_next_k, auto has_next) {
-    constexpr bool LK = decltype(load_next_k)::value;
-    constexpr bool NX = decltype(has_next)::value;
-    if constexpr (LK) load_k(tile_of(i + 2));
-    if constexpr (NX) load_v(tile_of(i + 1));
-    // Keep the loads at the top: their latency is covered by this iteration's MFMAs.
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto prob_pv = [&](int vbuf) {
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    if constexpr (NX) qk((i + 1) & 1, s_nxt);
     bf16x8 pf[4];
-    const float lsum = softmax(s_cur, m_use, pf);
-    pv(i & 1, pf);
+    const float lsum = softmax(sc, m_use, pf);
+    pv(vbuf, pf);
     l_run += lsum;
-    if constexpr (NX) {
-      const float mt_next = bias_max((i + 1) & 1, tile_of(i + 1), s_nxt);
-      const bool raise = mt_next > m_run + 8.0f;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-        const float m_new = raise ? mt_next : m_run;
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-        m_run = m_new;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (LK) store_k(i & 1);
-    if constexpr (NX) store_v((i + 1) & 1);
   };
 
-  for (int i = 0; i < n_iter; ++i) {
-    if (i + 2 < n_g) {
-      iteration(i, std::true_type{}, std::true_type{});
-    } else if (i + 1 < n_g) {
-      iteration(i, std::false_type{}, std::true_type{});
-    } else if (i < n_g) {
-      iteration(i, std::false_type{}, std::false_type{});
+  // ---- prologue.  Group 0 consumes K and V of tile i in iteration i; group 1
+  // runs one K tile ahead (its iteration i ends with the scores of tile i+1).
+  if (n_g > 0) {
+    fill(kbase, tile_of(0), k_off(0));
+    bias_of(tile_of(0));
+    store_bias(0);
+    fill(vbase, tile_of(0), v_off(0));
+    if (grp == 1 && n_g > 1) {
+      fill(kbase, tile_of(1), k_off(1));
+      bias_of(tile_of(1));
+      store_bias(1);
     }
-    __syncthreads();
-    s_cur[0] = s_nxt[0];
-    s_cur[1] = s_nxt[1];
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's LDS fills have landed
+  __syncthreads();
+
+  // ---- main loop; every wave runs n_iter iterations so that barriers match.
+  // On each SIMD one wave of each group runs; right after every barrier group 0
+  // is in its Q K^T MFMAs while group 1 is in its softmax VALU work, then the
+  // roles swap, so the matrix pipe and the VALU overlap across the two waves.
+  if (grp == 0) {
+    for (int i = 0; i < n_iter; ++i) {
+      if (i < n_g) {
+        const bool nx = i + 1 < n_g;
+        if (nx) {
+          fill(kbase, tile_of(i + 1), k_off((i + 1) & 1));
+          fill(vbase, tile_of(i + 1), v_off((i + 1) & 1));
+          bias_of(tile_of(i + 1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        qk(i & 1, sc);
+        rescale(bias_max(i & 1, tile_of(i), sc));
+        prob_pv(i & 1);
+        if (nx) store_bias((i + 1) & 1);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
+    }
+  } else {
+    if (n_g > 0) {
+      qk(0, sc);
+      m_run = bias_max(0, tile_of(0), sc);
+    }
+    for (int i = 0; i < n_iter; ++i) {
+      if (i < n_g) {
+        const bool nx = i + 1 < n_g, nk = i + 2 < n_g;
+        if (nk) {
+          fill(kbase, tile_of(i + 2), k_off(i & 1));
+          bias_of(tile_of(i + 2));
+        }
+        if (nx) fill(vbase, tile_of(i + 1), v_off((i + 1) & 1));
+        __builtin_amdgcn_sched_barrier(0);
+        prob_pv(i & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nx) {
+          qk((i + 1) & 1, sc);
+          rescale(bias_max((i + 1) & 1, tile_of(i + 1), sc));
+        }
+        if (nk) store_bias(i & 1);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
+    }
   }
 
-  // ---- merge the two groups' softmax states through LDS (reusing the K buffers)
-  float* comb = reinterpret_cast<float*>(&kbuf[0][0][0]);
+  // ---- merge the two groups' softmax states through LDS (reusing the tiles)
+  float* comb = reinterpret_cast<float*>(lds);
   auto slot = [&](int k) { return (gw * C::NCOMB + k) * 64 + lane; };
   if (grp == 1) {
 #pragma unroll
@@ -415,6 +424,11 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(AttnArgs a) {
         }
     }
   }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads) attn_fwd_kernel(AttnArgs a) {
+  attn_fwd_body<D>(a);
 }
 
 }  // namespace

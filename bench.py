@@ -24,8 +24,10 @@ all-gather), and the output reverse runs on a resident head-sharded buffer of th
 Ulysses layout.
 
 Prints one JSON line.  `value` is attention TFLOP/s over the whole step
-(algorithmic attention FLOPs / step time); per-kernel durations come from HIP
-events recorded around each launch on the launch stream.
+(algorithmic attention FLOPs / step time), with the step captured once into a
+HIP graph and replayed (`--eager` launches it op by op).  Per-kernel durations
+come from HIP events on the launch stream around bursts of back-to-back
+launches of each kernel on the step's own buffers.
 """
 
 from __future__ import annotations
@@ -57,6 +59,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=10.0)
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache pack/unpack pass")
+    p.add_argument("--eager", action="store_true",
+                   help="launch the timed steps one by one instead of replaying a captured HIP graph")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="run only a plain 256 MiB device copy (counter calibration for traffic)")
+    p.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
+                   help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench and of "
+                        "--calib-copy into a traffic summary; no GPU work")
     p.add_argument("--only", default=None,
                    help="profile aid: run only this kernel's launches in the timed loop "
                         "(pack|unpack|attn|merge); the JSON line is then not the headline")
@@ -226,17 +235,15 @@ def cold_layout_gbps(wl, dev, rounds=4):
         for sset in sets:
             launch(sset)
         torch.cuda.synchronize()
-        times = []
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
         for _ in range(rounds):
             for sset in sets:
-                s = torch.cuda.Event(enable_timing=True)
-                e = torch.cuda.Event(enable_timing=True)
-                s.record()
                 launch(sset)
-                e.record()
-                times.append((s, e))
+        e.record()
         torch.cuda.synchronize()
-        ms = float(np.median([s.elapsed_time(e) for s, e in times]))
+        ms = s.elapsed_time(e) / (rounds * len(sets))
         res.append(wl.pack_bytes() / (ms * 1e-3) / 1e9)
     del sets
     torch.cuda.empty_cache()
@@ -263,15 +270,21 @@ def cpu_baseline(wl, full, mask, budget_s):
         return 4.0 * wl.attn_heads * n * wl.D * float(mask.astype(np.int64).sum())
 
     n0 = min(wl.attn_rows, 16)
-    q0 = bf16.bits_to_f64(q_all[:, :n0])
+    OA.attention(bf16.bits_to_f64(q_all[:, :n0]), k, v, mask, 1.0 / math.sqrt(wl.D))   # warm-up
+    n1 = min(wl.attn_rows, 4 * n0)
+    q1 = bf16.bits_to_f64(q_all[:, :n1])
     t = time.perf_counter()
-    OA.attention(q0, k, v, mask, 1.0 / math.sqrt(wl.D))
-    t0 = time.perf_counter() - t
-    n = int(min(wl.attn_rows, max(n0, n0 * budget_s / max(t0, 1e-6))))
+    OA.attention(q1, k, v, mask, 1.0 / math.sqrt(wl.D))
+    t1 = time.perf_counter() - t
+    n = int(min(wl.attn_rows, max(n1, n1 * budget_s / max(t1, 1e-6))))
     q = bf16.bits_to_f64(q_all[:, :n])
+    # When the whole problem is quicker than the budget, repeat it (up to 30 times).
+    est = t1 * n / n1
+    reps = int(max(1, min(30, budget_s // max(est, 1e-6))))
     t = time.perf_counter()
-    OA.attention(q, k, v, mask, 1.0 / math.sqrt(wl.D))
-    dt = time.perf_counter() - t
+    for _ in range(reps):
+        OA.attention(q, k, v, mask, 1.0 / math.sqrt(wl.D))
+    dt = (time.perf_counter() - t) / reps
     threads = os.cpu_count()
     try:
         from threadpoolctl import threadpool_info
@@ -284,7 +297,7 @@ def cpu_baseline(wl, full, mask, budget_s):
     return {
         "value": flops(n) / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": f"fp64 oracle attention over query rows [0,{n}) of {wl.attn_rows}, "
-                  f"{wl.attn_heads} heads, all {wl.S} keys, B={wl.B}; {dt:.1f} s; "
+                  f"{wl.attn_heads} heads, all {wl.S} keys, B={wl.B}; {reps} pass(es) of {dt:.2f} s; "
                   f"host cpu_count={os.cpu_count()}",
     }
 
@@ -321,13 +334,101 @@ def parity_sample(path, wl, nrows=24):
     return res
 
 
+def kernel_bursts(path, only=None, burst=20):
+    """Average duration (ms) of each kernel of the step over `burst` back-to-back launches."""
+    import torch
+    snd = path.send()
+    launches = {
+        "pack": path.pack, "exchange_in": path.exchange_in, "unpack": path.unpack,
+        "attn": path.attn, "exchange_out": lambda: path.exchange_out(snd), "merge": path.merge,
+    }
+    if path.wl.B > 1:
+        launches["send"] = path.send
+    res = {}
+    for name, fn in launches.items():
+        if only is not None and name != only:
+            continue
+        fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(burst):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        res[name] = s.elapsed_time(e) / burst
+    return res
+
+
+ATTN_SRC = os.path.join(ROOT, "context_attention_diffusion_amd", "csrc", "cp_attention.hip")
+CALIB_BYTES = 256 << 20
+
+
+def src_sha256(path=ATTN_SRC):
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_attn_fwd_{workload}.json")
+
+
+def read_counter_csv(d, counter, kernel_substr):
+    """Mean per-dispatch value of `counter` for kernels whose name contains kernel_substr."""
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    return float(np.mean(vals)) if vals else None
+
+
+def summarize_traffic(fetch_dir, write_dir, out_json, workload):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, each scaled by
+    what the same counter reads for the calibration copy (CALIB_BYTES read, CALIB_BYTES written)."""
+    f_attn = read_counter_csv(os.path.join(fetch_dir, "attn"), "FETCH_SIZE", "attn_fwd")
+    w_attn = read_counter_csv(os.path.join(write_dir, "attn"), "WRITE_SIZE", "attn_fwd")
+    f_copy = read_counter_csv(os.path.join(fetch_dir, "copy"), "FETCH_SIZE", "copy")
+    w_copy = read_counter_csv(os.path.join(write_dir, "copy"), "WRITE_SIZE", "copy")
+    sf = (CALIB_BYTES / 1024.0) / f_copy
+    sw = (CALIB_BYTES / 1024.0) / w_copy
+    res = {"kernel": "attn_fwd_kernel", "workload": workload, "src_sha256": src_sha256(),
+           "fetch_kib_raw": f_attn, "write_kib_raw": w_attn,
+           "copy_fetch_kib_raw": f_copy, "copy_write_kib_raw": w_copy,
+           "scale_fetch": sf, "scale_write": sw,
+           "traffic_bytes": (f_attn * sf + w_attn * sw) * 1024.0}
+    with open(out_json, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res))
+
+
+def calib_copy():
+    import torch
+    a = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda:0").normal_()
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": CALIB_BYTES}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.workload)
+        return
     import torch
+
+    if args.calib_copy:
+        calib_copy()
+        return
 
     import workloads
 
@@ -338,22 +439,33 @@ def main():
         run_steps(path, 1, only=args.only)
     torch.cuda.synchronize()
 
+    graph = None
+    if not args.eager:
+        # One step captured into a HIP graph and replayed: the same kernels with
+        # the host launch overhead taken out of the step.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_steps(path, 1, only=args.only)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+
     # Timed region: exactly `steps` steps, synchronised on both sides.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run_steps(path, args.steps, only=args.only)
+    if graph is not None:
+        for _ in range(args.steps):
+            graph.replay()
+    else:
+        run_steps(path, args.steps, only=args.only)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # Per-kernel durations from HIP events on the launch stream, over a second pass
-    # of the same steps (the events would otherwise perturb the step clock).
-    events = []
-    run_steps(path, args.steps, events=events, only=args.only)
-    torch.cuda.synchronize()
-    kms = {}
-    for name in events[0]:
-        kms[name] = float(np.mean([rec[name][0].elapsed_time(rec[name][1]) for rec in events]))
+    # Per-kernel durations: each kernel of the step launched `burst` times back to
+    # back on the launch stream between one pair of HIP events (same buffers as the
+    # step), so the event overhead is amortised.
+    kms = kernel_bursts(path, only=args.only, burst=max(5, min(50, args.steps)))
 
     flops = attn_flops(wl, path.mask_np)
     pack_bytes, merge_bytes = wl.pack_bytes(), wl.merge_bytes()
@@ -370,8 +482,6 @@ def main():
             t = kms[name] * 1e-3
             kern[name] = {"us": kms[name] * 1e3, "GBps_warm": nbytes / t / 1e9,
                           "frac_hbm_peak": nbytes / t / 1e9 / PEAK_HBM_GBPS, "bytes": nbytes}
-    if wl.B == 1 and "send" in kern:
-        kern["send"]["note"] = "identity layout for B=1: no kernel"
 
     value = flops / (ms_per_step * 1e-3) / 1e12 if args.only in (None, "attn") else None
     out = {
@@ -382,6 +492,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "launch": "eager" if graph is None else "hip_graph_replay",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -394,10 +505,17 @@ def main():
                    "parallelism": "one rank's share, exchange simulated on one GPU"},
     }
     if "attn" in kern:
+        traffic = None
+        tf = traffic_file(wl.name)
+        if os.path.exists(tf):
+            t = json.load(open(tf))
+            if t.get("src_sha256") == src_sha256():   # counters taken on this kernel source
+                traffic = t["traffic_bytes"]
         out["roofline"] = {"bound": "mfma", "achieved": kern["attn"]["TFLOPs"],
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": kern["attn"]["TFLOPs"] / PEAK_BF16_TFLOPS, "traffic": None,
-                           "kernel": "attn_fwd_kernel"}
+                           "frac": kern["attn"]["TFLOPs"] / PEAK_BF16_TFLOPS, "traffic": traffic,
+                           "kernel": "attn_fwd_kernel",
+                           "algorithmic_flops_per_launch": flops}
     out["kernels"] = kern
     if args.only is None and not args.no_cold:
         pc, uc = cold_layout_gbps(wl, dev)

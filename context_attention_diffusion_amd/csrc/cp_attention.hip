@@ -177,6 +177,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     const int chunk = (slot % C::CHUNKS) ^ C::swz(key);
     goff[j] = uint32_t(key) * rs_bytes + uint32_t(chunk) * 16u;
   }
+  // lds_off: byte offset of the destination tile (any group's buffer).
   auto fill = [&](const __bf16* base, int t, int lds_off) {
     const uint32_t off = uint32_t(t) * uint32_t(C::BN) * rs_bytes;
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -187,22 +188,27 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsrc, (lds_void*)(lds + lds_off + (gw * C::SPT + j) * 1024), 16, goff[j], 0, 0, 0);
   };
-  auto k_off = [&](int buf) { return C::K_OFF + (grp * 2 + buf) * C::TILE; };
-  auto v_off = [&](int buf) { return C::V_OFF + (grp * 2 + buf) * C::TILE; };
+  auto k_off_of = [&](int g, int buf) { return C::K_OFF + (g * 2 + buf) * C::TILE; };
+  auto v_off_of = [&](int g, int buf) { return C::V_OFF + (g * 2 + buf) * C::TILE; };
+  auto k_off = [&](int buf) { return k_off_of(grp, buf); };
+  auto v_off = [&](int buf) { return v_off_of(grp, buf); };
+  const int n_g1 = n_tiles / 2;   // tiles of group 1 (local tile i is global tile 2i + 1)
   float* bias_row = reinterpret_cast<float*>(lds + C::BIAS_OFF) + grp * 2 * C::BN;
 
   // Key validity of tile t as an additive bias, one key per thread of wave 0.
-  float breg = 0.f;
+  // The mask byte is loaded here and only compared when the bias row is
+  // stored, late in the iteration, so its load latency is never waited on early.
+  bool kvalid = true;
+  uint32_t mraw = 1;
   auto bias_of = [&](int t) {
     if (gt < C::BN) {
       const int key = t * C::BN + gt;
-      bool valid = key < a.Skv;
-      if (mbase) valid = valid && mbase[valid ? key : 0] != 0;
-      breg = valid ? 0.f : -INFINITY;
+      kvalid = key < a.Skv;
+      mraw = mbase ? uint32_t(mbase[kvalid ? key : 0]) : 1u;
     }
   };
   auto store_bias = [&](int buf) {
-    if (gt < C::BN) bias_row[buf * C::BN + gt] = breg;
+    if (gt < C::BN) bias_row[buf * C::BN + gt] = (kvalid && mraw != 0) ? 0.f : -INFINITY;
   };
 
   // ---- LDS readers
@@ -323,16 +329,27 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 
   // ---- prologue.  Group 0 consumes K and V of tile i in iteration i; group 1
   // runs one K tile ahead (its iteration i ends with the scores of tile i+1).
+  // Only group 0 issues HBM->LDS fills, for both groups' buffers: fill
+  // instructions stall at issue while the texture path drains, and group 1 is
+  // the one on the critical path.
+  if (grp == 0) {
+    if (n_g > 0) {
+      fill(kbase, 2 * 0 + 0, k_off_of(0, 0));
+      fill(vbase, 2 * 0 + 0, v_off_of(0, 0));
+    }
+    if (n_g1 > 0) {
+      fill(kbase, 2 * 0 + 1, k_off_of(1, 0));
+      fill(vbase, 2 * 0 + 1, v_off_of(1, 0));
+    }
+    if (n_g1 > 1) fill(kbase, 2 * 1 + 1, k_off_of(1, 1));
+  }
   if (n_g > 0) {
-    fill(kbase, tile_of(0), k_off(0));
     bias_of(tile_of(0));
     store_bias(0);
-    fill(vbase, tile_of(0), v_off(0));
-    if (grp == 1 && n_g > 1) {
-      fill(kbase, tile_of(1), k_off(1));
-      bias_of(tile_of(1));
-      store_bias(1);
-    }
+  }
+  if (grp == 1 && n_g > 1) {
+    bias_of(tile_of(1));
+    store_bias(1);
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's LDS fills have landed
   __syncthreads();
@@ -346,10 +363,13 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       if (i < n_g) {
         const bool nx = i + 1 < n_g;
         if (nx) {
-          fill(kbase, tile_of(i + 1), k_off((i + 1) & 1));
-          fill(vbase, tile_of(i + 1), v_off((i + 1) & 1));
+          fill(kbase, 2 * (i + 1), k_off_of(0, (i + 1) & 1));
+          fill(vbase, 2 * (i + 1), v_off_of(0, (i + 1) & 1));
           bias_of(tile_of(i + 1));
         }
+        // group 1's next K (two tiles ahead) and V (one tile ahead)
+        if (i + 2 < n_g1) fill(kbase, 2 * (i + 2) + 1, k_off_of(1, i & 1));
+        if (i + 1 < n_g1) fill(vbase, 2 * (i + 1) + 1, v_off_of(1, (i + 1) & 1));
         __builtin_amdgcn_sched_barrier(0);
         qk(i & 1, sc);
         rescale(bias_max(i & 1, tile_of(i), sc));
@@ -367,11 +387,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     for (int i = 0; i < n_iter; ++i) {
       if (i < n_g) {
         const bool nx = i + 1 < n_g, nk = i + 2 < n_g;
-        if (nk) {
-          fill(kbase, tile_of(i + 2), k_off(i & 1));
-          bias_of(tile_of(i + 2));
-        }
-        if (nx) fill(vbase, tile_of(i + 1), v_off((i + 1) & 1));
+        if (nk) bias_of(tile_of(i + 2));
         __builtin_amdgcn_sched_barrier(0);
         prob_pv(i & 1);
         __builtin_amdgcn_sched_barrier(0);

@@ -26,8 +26,8 @@ Ulysses layout.
 Prints one JSON line.  `value` is attention TFLOP/s over the whole step
 (algorithmic attention FLOPs / step time), with the step captured once into a
 HIP graph and replayed (`--eager` launches it op by op).  Per-kernel durations
-come from HIP events on the launch stream around bursts of back-to-back
-launches of each kernel on the step's own buffers.
+come from HIP events on the launch stream around a HIP-graph replay of a burst
+of back-to-back launches of each kernel on the step's own buffers.
 """
 
 from __future__ import annotations
@@ -135,6 +135,12 @@ class RankPath:
         self.out = torch.empty((B, Sl, H, D), dtype=torch.bfloat16, device=dev)
         self.full = full
         self.mask_np = mask
+        # Fill every intermediate buffer with real data once, so that a run that
+        # times only some of the kernels still feeds them the workload's values.
+        self.pack()
+        self.exchange_in()
+        self.unpack()
+        torch.cuda.synchronize()
 
     # -- the launches of one step
     def pack(self):
@@ -235,15 +241,9 @@ def cold_layout_gbps(wl, dev, rounds=4):
         for sset in sets:
             launch(sset)
         torch.cuda.synchronize()
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(rounds):
-            for sset in sets:
-                launch(sset)
-        e.record()
-        torch.cuda.synchronize()
-        ms = s.elapsed_time(e) / (rounds * len(sets))
+        order = [sets[i % len(sets)] for i in range(rounds * len(sets))]
+        it = iter(order * 2)
+        ms = time_burst(lambda: launch(next(it)), len(order))
         res.append(wl.pack_bytes() / (ms * 1e-3) / 1e9)
     del sets
     torch.cuda.empty_cache()
@@ -334,9 +334,30 @@ def parity_sample(path, wl, nrows=24):
     return res
 
 
+def time_burst(fn, burst):
+    """Average duration (ms) of `fn` over `burst` back-to-back launches: the burst is
+    captured once into a HIP graph and its replay is timed with HIP events on the
+    launch stream, so host launch overhead does not enter the figure."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(burst):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    graph.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / burst
+
+
 def kernel_bursts(path, only=None, burst=20):
     """Average duration (ms) of each kernel of the step over `burst` back-to-back launches."""
-    import torch
     snd = path.send()
     launches = {
         "pack": path.pack, "exchange_in": path.exchange_in, "unpack": path.unpack,
@@ -348,16 +369,7 @@ def kernel_bursts(path, only=None, burst=20):
     for name, fn in launches.items():
         if only is not None and name != only:
             continue
-        fn()
-        torch.cuda.synchronize()
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(burst):
-            fn()
-        e.record()
-        torch.cuda.synchronize()
-        res[name] = s.elapsed_time(e) / burst
+        res[name] = time_burst(fn, burst)
     return res
 
 

@@ -7,11 +7,19 @@
 // usp.py excerpt of _usp_input_all_to_all_qkv and the unit-test excerpt); the
 // output reverse is read as the inverse of the forward exchange.
 //
-// Kernel shape (all four maps): HBM-bound permutations of contiguous runs.  Each
-// thread owns kVecPerThread output vectors spaced one block apart, issues all
-// their loads before any store (bytes in flight), and writes the output in
-// order so stores are fully coalesced; reads come in runs of D*2 bytes (pack,
-// unpack) or H_local*D*2 bytes (reverse), >= 128 B for every supported shape.
+// Kernel shape: all four maps are HBM-bound permutations of contiguous runs and
+// share one persistent kernel.  A map object gives the source and destination
+// of each 16-byte vector; blocks (8 per CU) stride over tiles of 1024 vectors
+// and each thread loads its 4 vectors of the next tile before storing those of
+// the current one, so reads and writes stay in flight together.  Pack, reverse
+// and exchange enumerate the output in order (coalesced stores, reads in runs of
+// D*2 or H_local*D*2 bytes); unpack enumerates its input in order (sequential
+// reads, writes in D*2-byte runs).  Loads use the default cache policy (the
+// sources are usually still cache-resident).  Stores are nontemporal only where
+// the result leaves for the collective (pack staging, reverse send layout);
+// results that the next kernel reads (unpacked Q/K/V, the receive buffer, the
+// merged output) are stored with the default policy: K/V written nontemporally
+// are markedly slower for the attention kernel's repeated reads.
 
 #include <hip/hip_runtime.h>
 
@@ -23,153 +31,174 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kVecPerThread = 4;
 constexpr int kVecPerBlock = kThreads * kVecPerThread;
+constexpr int kBlocksPerCu = 8;
 
 typedef uint32_t vec_t __attribute__((ext_vector_type(4)));  // 16 bytes
 
-__device__ __forceinline__ vec_t ld(const vec_t* p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ void st(vec_t* p, vec_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ vec_t ld(const vec_t* p) { return *p; }
+template <bool NT>
+__device__ __forceinline__ void st(vec_t* p, vec_t v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 
-// ------------------------------------------------------------------ pack
-// Output order (j, row, hl, c, dv); VD = D/8 vectors per head row.
+// ------------------------------------------------------------------ the one kernel
+// Every layout map is a permutation of 16-byte vectors given by a map object:
+// m.src(o) / m.dst(o) for output-ordered index o.  Blocks stride over tiles of
+// kVecPerBlock vectors; each thread loads its 4 vectors of the next tile before
+// storing those of the current one, so reads and writes stay in flight together.
+template <class Map, bool NT_STORE>
+__global__ void __launch_bounds__(kThreads) permute_kernel(Map m, uint32_t n_vec) {
+  const uint32_t n_tiles = (n_vec + kVecPerBlock - 1) / kVecPerBlock;
+  uint32_t tile = blockIdx.x;
+  if (tile >= n_tiles) return;
+  vec_t cur[kVecPerThread];
+  auto load = [&](uint32_t t, vec_t* buf) {
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const uint32_t o = t * kVecPerBlock + u * kThreads + threadIdx.x;
+      if (o < n_vec) buf[u] = ld(m.src(o));
+    }
+  };
+  auto store = [&](uint32_t t, const vec_t* buf) {
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const uint32_t o = t * kVecPerBlock + u * kThreads + threadIdx.x;
+      if (o < n_vec) st<NT_STORE>(m.dst(o), buf[u]);
+    }
+  };
+  load(tile, cur);
+  for (;;) {
+    const uint32_t nxt = tile + gridDim.x;
+    vec_t nb[kVecPerThread];
+    if (nxt < n_tiles) load(nxt, nb);
+    store(tile, cur);
+    if (nxt >= n_tiles) break;
+    tile = nxt;
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) cur[u] = nb[u];
+  }
+}
+
+// ------------------------------------------------------------------ maps
+// pack: output order (j, row, hl, c, dv); VD = D/8 vectors per head row (0 = runtime vd).
 template <int VD>
-__global__ void __launch_bounds__(kThreads)
-pack_kernel(const vec_t* __restrict__ q, const vec_t* __restrict__ k,
-            const vec_t* __restrict__ v, vec_t* __restrict__ out, uint32_t n_vec,
-            uint32_t vd_rt, FastDiv div_vd, FastDiv div_hl, FastDiv div_rows,
-            uint32_t H_local, uint32_t H) {
-  const uint32_t vd = VD > 0 ? uint32_t(VD) : vd_rt;
-  const uint32_t base = blockIdx.x * kVecPerBlock + threadIdx.x;
-  vec_t buf[kVecPerThread];
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u) {
-    const uint32_t o = base + u * kThreads;
-    if (o < n_vec) {
-      uint32_t t, dv;
-      if (VD > 0) { dv = o % VD; t = o / VD; } else { div_vd.divmod(o, t, dv); }
-      const uint32_t c = t % 3u;
-      t /= 3u;
-      uint32_t rj, hl, j, row;
-      div_hl.divmod(t, rj, hl);
-      div_rows.divmod(rj, j, row);
-      const vec_t* src = c == 0 ? q : (c == 1 ? k : v);
-      buf[u] = ld(src + (size_t(row) * H + j * H_local + hl) * vd + dv);
-    }
+struct PackMap {
+  // the staging buffer goes to the collective, not to another kernel on this GPU
+  static constexpr bool kNontemporalStore = true;
+  const vec_t *q, *k, *v;
+  vec_t* out;
+  uint32_t vd, H_local, H;
+  FastDiv div_vd, div_hl, div_rows;
+  __device__ __forceinline__ const vec_t* src(uint32_t o) const {
+    uint32_t t, dv;
+    if (VD > 0) { dv = o % VD; t = o / VD; } else { div_vd.divmod(o, t, dv); }
+    const uint32_t c = t % 3u;
+    t /= 3u;
+    uint32_t rj, hl, j, row;
+    div_hl.divmod(t, rj, hl);
+    div_rows.divmod(rj, j, row);
+    const vec_t* base = c == 0 ? q : (c == 1 ? k : v);
+    const uint32_t w = VD > 0 ? uint32_t(VD) : vd;
+    return base + (size_t(row) * H + j * H_local + hl) * w + dv;
   }
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u) {
-    const uint32_t o = base + u * kThreads;
-    if (o < n_vec) st(out + o, buf[u]);
-  }
-}
-
-// ------------------------------------------------------------------ unpack
-// Output order (c, b, t, hl, dv) over the three outputs, t = r*S_local + s.
-template <int VD>
-__global__ void __launch_bounds__(kThreads)
-unpack_kernel(const vec_t* __restrict__ recv, vec_t* __restrict__ q, vec_t* __restrict__ k,
-              vec_t* __restrict__ v, uint32_t n_vec_per_out, uint32_t vd_rt,
-              FastDiv div_inner, FastDiv div_wsl, FastDiv div_sl, FastDiv div_b,
-              uint32_t rows, uint32_t H_local) {
-  const uint32_t vd = VD > 0 ? uint32_t(VD) : vd_rt;
-  const uint32_t n_vec = 3u * n_vec_per_out;
-  const uint32_t base = blockIdx.x * kVecPerBlock + threadIdx.x;
-  vec_t buf[kVecPerThread];
-  vec_t* dst[kVecPerThread];
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u) {
-    const uint32_t o = base + u * kThreads;
-    dst[u] = nullptr;
-    if (o < n_vec) {
-      uint32_t run, inner;
-      div_inner.divmod(o, run, inner);                 // inner over (hl, dv)
-      uint32_t hl, dv;
-      if (VD > 0) { hl = inner / VD; dv = inner % VD; } else { hl = inner / vd; dv = inner % vd; }
-      uint32_t bc, t, r, s, c, b;
-      div_wsl.divmod(run, bc, t);                      // run = bc * (W*S_l) + t
-      div_sl.divmod(t, r, s);
-      div_b.divmod(bc, c, b);
-      const uint32_t row = b * div_sl.d + s;
-      buf[u] = ld(recv + ((size_t(r) * rows + row) * H_local + hl) * (3u * vd) + c * vd + dv);
-      vec_t* base_out = c == 0 ? q : (c == 1 ? k : v);
-      dst[u] = base_out + (o - c * n_vec_per_out);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u)
-    if (dst[u]) st(dst[u], buf[u]);
-}
-
-// ------------------------------------------------------------------ reverse
-// Both phases copy runs of `run` vectors (H_local * D / 8).
-//   SEND : out (r, b, s)  <- src (b, r*S_l + s)
-//   MERGE: out (b, s, j)  <- src (j, b, s)
-template <int PHASE>
-__global__ void __launch_bounds__(kThreads)
-reverse_kernel(const vec_t* __restrict__ src, vec_t* __restrict__ out, uint32_t n_vec,
-               FastDiv div_run, FastDiv div_a, FastDiv div_b, uint32_t W, uint32_t B,
-               uint32_t S_local) {
-  const uint32_t base = blockIdx.x * kVecPerBlock + threadIdx.x;
-  const uint32_t run = div_run.d;
-  vec_t buf[kVecPerThread];
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u) {
-    const uint32_t o = base + u * kThreads;
-    if (o < n_vec) {
-      uint32_t idx, inner;
-      div_run.divmod(o, idx, inner);
-      size_t src_run;
-      if (PHASE == 0) {
-        // idx = (r * B + b) * S_l + s ; div_a = S_l, div_b = B
-        uint32_t rb, s, r, b;
-        div_a.divmod(idx, rb, s);
-        div_b.divmod(rb, r, b);
-        src_run = (size_t(b) * W + r) * S_local + s;
-      } else {
-        // idx = (b * S_l + s) * W + j ; div_a = W, div_b = S_l
-        uint32_t bs, j, b, s;
-        div_a.divmod(idx, bs, j);
-        div_b.divmod(bs, b, s);
-        src_run = (size_t(j) * B + b) * S_local + s;
-      }
-      buf[u] = ld(src + src_run * run + inner);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u) {
-    const uint32_t o = base + u * kThreads;
-    if (o < n_vec) st(out + o, buf[u]);
-  }
-}
-
-// ------------------------------------------------------------------ simulated exchange
-constexpr int kMaxRanks = 64;
-struct SendPtrs {
-  const vec_t* p[kMaxRanks];
+  __device__ __forceinline__ vec_t* dst(uint32_t o) const { return out + o; }
 };
 
-__global__ void __launch_bounds__(kThreads)
-exchange_kernel(SendPtrs sends, vec_t* __restrict__ recv, uint32_t n_vec, FastDiv div_chunk,
-                uint32_t rank) {
-  const uint32_t base = blockIdx.x * kVecPerBlock + threadIdx.x;
-  const uint32_t chunk = div_chunk.d;
-  vec_t buf[kVecPerThread];
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u) {
-    const uint32_t o = base + u * kThreads;
-    if (o < n_vec) {
-      uint32_t r, e;
-      div_chunk.divmod(o, r, e);
-      buf[u] = ld(sends.p[r] + size_t(rank) * chunk + e);
+// unpack: input order (r, row = b*S_l + s, hl, c, dv) over the receive buffer, so reads
+// are sequential; the vector goes to out_c[b][r*S_l + s][hl][dv].
+template <int VD>
+struct UnpackMap {
+  // Q/K/V are read next (K/V many times) by the attention kernel: keep them cacheable
+  static constexpr bool kNontemporalStore = false;
+  const vec_t* recv;
+  vec_t *q, *k, *v;
+  uint32_t vd, H_local, wsl;                  // wsl = W * S_local output rows per batch
+  FastDiv div_3vd, div_hl, div_sl, div_rows;
+  __device__ __forceinline__ const vec_t* src(uint32_t o) const { return recv + o; }
+  __device__ __forceinline__ vec_t* dst(uint32_t o) const {
+    const uint32_t w = VD > 0 ? uint32_t(VD) : vd;
+    uint32_t t, e;
+    div_3vd.divmod(o, t, e);  // e = c*w + dv
+    const uint32_t c = e / w, dv = e % w;
+    uint32_t rr, hl, r, row, b, s;
+    div_hl.divmod(t, rr, hl);  // rr = r*rows + row
+    div_rows.divmod(rr, r, row);
+    div_sl.divmod(row, b, s);
+    vec_t* base = c == 0 ? q : (c == 1 ? k : v);
+    return base + ((size_t(b) * wsl + r * div_sl.d + s) * H_local + hl) * w + dv;
+  }
+};
+
+// reverse: runs of `run` vectors.  SEND: out (r, b, s) <- src (b, r*S_l + s);
+// MERGE: out (b, s, j) <- src (j, b, s).
+template <int PHASE>
+struct ReverseMap {
+  static constexpr bool kNontemporalStore = PHASE == 0;  // send layout goes to the collective
+  const vec_t* src_;
+  vec_t* out;
+  uint32_t W, B, S_local;
+  FastDiv div_run, div_a, div_b;
+  __device__ __forceinline__ const vec_t* src(uint32_t o) const {
+    uint32_t idx, inner;
+    div_run.divmod(o, idx, inner);
+    size_t src_run;
+    if (PHASE == 0) {
+      uint32_t rb, s, r, b;  // idx = (r * B + b) * S_l + s
+      div_a.divmod(idx, rb, s);
+      div_b.divmod(rb, r, b);
+      src_run = (size_t(b) * W + r) * S_local + s;
+    } else {
+      uint32_t bs, j, b, s;  // idx = (b * S_l + s) * W + j
+      div_a.divmod(idx, bs, j);
+      div_b.divmod(bs, b, s);
+      src_run = (size_t(j) * B + b) * S_local + s;
     }
+    return src_ + src_run * div_run.d + inner;
   }
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u) {
-    const uint32_t o = base + u * kThreads;
-    if (o < n_vec) st(recv + o, buf[u]);
+  __device__ __forceinline__ vec_t* dst(uint32_t o) const { return out + o; }
+};
+
+// simulated exchange: recv chunk r <- chunk `rank` of sends[r].
+constexpr int kMaxRanks = 64;
+struct ExchangeMap {
+  static constexpr bool kNontemporalStore = false;  // the receive buffer is unpacked next
+  const vec_t* p[kMaxRanks];
+  vec_t* recv;
+  uint32_t rank;
+  FastDiv div_chunk;
+  __device__ __forceinline__ const vec_t* src(uint32_t o) const {
+    uint32_t r, e;
+    div_chunk.divmod(o, r, e);
+    return p[r] + size_t(rank) * div_chunk.d + e;
   }
+  __device__ __forceinline__ vec_t* dst(uint32_t o) const { return recv + o; }
+};
+
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
-inline unsigned grid_for(uint32_t n_vec) { return (n_vec + kVecPerBlock - 1) / kVecPerBlock; }
+inline unsigned grid_for(uint32_t n_vec) {
+  const unsigned tiles = (n_vec + kVecPerBlock - 1) / kVecPerBlock;
+  const unsigned cap = unsigned(num_cus()) * kBlocksPerCu;
+  return tiles < cap ? tiles : cap;
+}
+
+template <class Map>
+int launch_permute(const Map& m, uint32_t n_vec, hipStream_t s) {
+  hipLaunchKernelGGL((permute_kernel<Map, Map::kNontemporalStore>), dim3(grid_for(n_vec)), dim3(kThreads), 0, s,
+                     m, n_vec);
+  return hip_status(hipGetLastError());
+}
 
 // Shared checks of the layout entry points: sizes >= 1, D a multiple of 8.
 int check_layout_dims(int64_t B, int64_t S_local, int64_t H, int64_t D, int64_t W, int dtype) {
@@ -209,17 +238,14 @@ extern "C" int cp_pack_qkv_dst_major(const void* q, const void* k, const void* v
   const auto* kv = static_cast<const vec_t*>(k);
   const auto* vv = static_cast<const vec_t*>(v);
   auto* out = static_cast<vec_t*>(staging);
-  const dim3 grid(grid_for(uint32_t(n_vec))), block(kThreads);
   if (vd == 16)
-    hipLaunchKernelGGL(pack_kernel<16>, grid, block, 0, s, qv, kv, vv, out, uint32_t(n_vec), vd,
-                       dvd, dhl, drows, H_local, uint32_t(H));
-  else if (vd == 8)
-    hipLaunchKernelGGL(pack_kernel<8>, grid, block, 0, s, qv, kv, vv, out, uint32_t(n_vec), vd,
-                       dvd, dhl, drows, H_local, uint32_t(H));
-  else
-    hipLaunchKernelGGL(pack_kernel<0>, grid, block, 0, s, qv, kv, vv, out, uint32_t(n_vec), vd,
-                       dvd, dhl, drows, H_local, uint32_t(H));
-  return hip_status(hipGetLastError());
+    return launch_permute(PackMap<16>{qv, kv, vv, out, vd, H_local, uint32_t(H), dvd, dhl, drows},
+                          uint32_t(n_vec), s);
+  if (vd == 8)
+    return launch_permute(PackMap<8>{qv, kv, vv, out, vd, H_local, uint32_t(H), dvd, dhl, drows},
+                          uint32_t(n_vec), s);
+  return launch_permute(PackMap<0>{qv, kv, vv, out, vd, H_local, uint32_t(H), dvd, dhl, drows},
+                        uint32_t(n_vec), s);
 }
 
 extern "C" int cp_unpack_head_sharded(const void* recv, void* q_out, void* k_out, void* v_out,
@@ -242,24 +268,21 @@ extern "C" int cp_unpack_head_sharded(const void* recv, void* q_out, void* k_out
       overlaps(q_out, ob, v_out, ob) || overlaps(k_out, ob, v_out, ob))
     return CP_ERR_ALIAS;
   const uint32_t vd = uint32_t(D / 8);
-  FastDiv dinner{uint32_t(H_local) * vd}, dwsl{uint32_t(wsl)}, dsl{uint32_t(S_local)},
-      db{uint32_t(B)};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const auto* rv = static_cast<const vec_t*>(recv);
   auto* qo = static_cast<vec_t*>(q_out);
   auto* ko = static_cast<vec_t*>(k_out);
   auto* vo = static_cast<vec_t*>(v_out);
-  const dim3 grid(grid_for(uint32_t(n_vec))), block(kThreads);
+  const FastDiv d3vd{3u * vd}, dhl{uint32_t(H_local)}, dsl{uint32_t(S_local)}, drows{uint32_t(rows)};
+  const uint32_t hl32 = uint32_t(H_local), wsl32 = uint32_t(wsl);
   if (vd == 16)
-    hipLaunchKernelGGL(unpack_kernel<16>, grid, block, 0, s, rv, qo, ko, vo, uint32_t(per_out), vd,
-                       dinner, dwsl, dsl, db, uint32_t(rows), uint32_t(H_local));
-  else if (vd == 8)
-    hipLaunchKernelGGL(unpack_kernel<8>, grid, block, 0, s, rv, qo, ko, vo, uint32_t(per_out), vd,
-                       dinner, dwsl, dsl, db, uint32_t(rows), uint32_t(H_local));
-  else
-    hipLaunchKernelGGL(unpack_kernel<0>, grid, block, 0, s, rv, qo, ko, vo, uint32_t(per_out), vd,
-                       dinner, dwsl, dsl, db, uint32_t(rows), uint32_t(H_local));
-  return hip_status(hipGetLastError());
+    return launch_permute(UnpackMap<16>{rv, qo, ko, vo, vd, hl32, wsl32, d3vd, dhl, dsl, drows},
+                          uint32_t(n_vec), s);
+  if (vd == 8)
+    return launch_permute(UnpackMap<8>{rv, qo, ko, vo, vd, hl32, wsl32, d3vd, dhl, dsl, drows},
+                          uint32_t(n_vec), s);
+  return launch_permute(UnpackMap<0>{rv, qo, ko, vo, vd, hl32, wsl32, d3vd, dhl, dsl, drows},
+                        uint32_t(n_vec), s);
 }
 
 extern "C" int cp_output_reverse(int phase, const void* src, void* dst, int64_t B,
@@ -278,17 +301,14 @@ extern "C" int cp_output_reverse(int phase, const void* src, void* dst, int64_t 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const auto* sv = static_cast<const vec_t*>(src);
   auto* dv = static_cast<vec_t*>(dst);
-  const dim3 grid(grid_for(uint32_t(n_vec))), block(kThreads);
   FastDiv drun{uint32_t(run)};
   if (phase == 0)
-    hipLaunchKernelGGL(reverse_kernel<0>, grid, block, 0, s, sv, dv, uint32_t(n_vec), drun,
-                       FastDiv(uint32_t(S_local)), FastDiv(uint32_t(B)), uint32_t(W), uint32_t(B),
-                       uint32_t(S_local));
-  else
-    hipLaunchKernelGGL(reverse_kernel<1>, grid, block, 0, s, sv, dv, uint32_t(n_vec), drun,
-                       FastDiv(uint32_t(W)), FastDiv(uint32_t(S_local)), uint32_t(W), uint32_t(B),
-                       uint32_t(S_local));
-  return hip_status(hipGetLastError());
+    return launch_permute(ReverseMap<0>{sv, dv, uint32_t(W), uint32_t(B), uint32_t(S_local), drun,
+                                        FastDiv(uint32_t(S_local)), FastDiv(uint32_t(B))},
+                          uint32_t(n_vec), s);
+  return launch_permute(ReverseMap<1>{sv, dv, uint32_t(W), uint32_t(B), uint32_t(S_local), drun,
+                                      FastDiv(uint32_t(W)), FastDiv(uint32_t(S_local))},
+                        uint32_t(n_vec), s);
 }
 
 extern "C" int cp_sim_exchange(const void* const* sends, void* recv, int64_t W, int64_t rank,
@@ -300,7 +320,7 @@ extern "C" int cp_sim_exchange(const void* const* sends, void* recv, int64_t W, 
   if (bytes_per_rank % (16 * W) != 0) return CP_ERR_DIVISIBILITY;
   if (bytes_per_rank / 16 > kMaxVectors) return CP_ERR_SHAPE;
   if (!aligned16(recv)) return CP_ERR_ALIGNMENT;
-  SendPtrs p{};
+  ExchangeMap p{};
   for (int64_t r = 0; r < W; ++r) {
     if (!sends[r]) return CP_ERR_NULL;
     if (!aligned16(sends[r])) return CP_ERR_ALIGNMENT;
@@ -310,8 +330,8 @@ extern "C" int cp_sim_exchange(const void* const* sends, void* recv, int64_t W, 
   }
   const uint32_t n_vec = uint32_t(bytes_per_rank / 16);
   const uint32_t chunk = n_vec / uint32_t(W);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(exchange_kernel, dim3(grid_for(n_vec)), dim3(kThreads), 0, s, p,
-                     static_cast<vec_t*>(recv), n_vec, FastDiv(chunk), uint32_t(rank));
-  return hip_status(hipGetLastError());
+  p.recv = static_cast<vec_t*>(recv);
+  p.rank = uint32_t(rank);
+  p.div_chunk = FastDiv(chunk);
+  return launch_permute(p, n_vec, reinterpret_cast<hipStream_t>(stream));
 }

@@ -16,7 +16,9 @@
 //    that write LDS directly (no VGPR staging), row-major, with the 16-byte
 //    chunks of each row XOR-swizzled so that both readers below are free of
 //    bank conflicts.  Rows past the last key fall outside the buffer
-//    descriptor's range and arrive as zeros.
+//    descriptor's range and arrive as zeros.  Each (operand, group, buffer)
+//    tile is its own LDS object, so the compiler can tell that the reads of one
+//    buffer do not wait on the in-flight fills of another.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16.  With keys as the MFMA row
 //    dimension, each lane owns one query column and 16 key rows per 32x32
 //    block, so the row max and row sum are in-lane reductions plus one
@@ -46,6 +48,7 @@
 
 #include <cmath>
 #include <type_traits>
+#include <utility>
 
 #include "cp_common.hpp"
 
@@ -78,13 +81,9 @@ struct Cfg {
   static constexpr int DB = D / 32;             // 32-row blocks of O^T
   static constexpr int KS = D / 16;             // 16-wide reduction steps of Q K^T
   static constexpr int NCOMB = DB * 16 + 2;     // floats per lane in the group merge
-  // LDS bytes: K tiles [group][buf], V tiles [group][buf], bias rows [group][buf][BN]
-  static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = kGroups * 2 * TILE;
-  static constexpr int BIAS_OFF = 2 * kGroups * 2 * TILE;
-  static constexpr int LDS_BYTES = BIAS_OFF + kGroups * 2 * BN * 4;
   static_assert(SPT * kGroupThreads * 16 == TILE, "tile must split evenly into slots");
-  static_assert(kGroupWaves * 64 * NCOMB * 4 <= BIAS_OFF, "group merge must fit in the tiles");
+  static_assert(64 * DB * 16 * 4 <= TILE, "a wave's O must fit in one tile array for the merge");
+  static_assert(kGroupWaves * 2 * 64 * 4 <= TILE, "m and l of the merge must fit in one tile array");
   // Chunk swizzle of a row (the 16-byte chunk index is XORed with it).  LDS
   // serves 16 lanes of a 16-byte read, or 32 lanes of an 8-byte read, per pass
   // over its 256 bytes of banks; the swizzle makes both passes conflict-free:
@@ -117,7 +116,12 @@ struct AttnArgs {
 template <int D>
 __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
+  // K and V tiles: one array per (operand, key group, buffer).  Separate objects
+  // let the compiler see that a fill of one buffer does not alias the reads of
+  // another, so no wait for the in-flight fills is inserted before those reads.
+  __shared__ __attribute__((aligned(1024))) char k00[C::TILE], k01[C::TILE], k10[C::TILE], k11[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char v00[C::TILE], v01[C::TILE], v10[C::TILE], v11[C::TILE];
+  __shared__ __attribute__((aligned(16))) float bias_all[kGroups * 2 * C::BN];
 
   // ---- XCD-aware work numbering: consecutive logical tiles share an XCD.
   const int pid = blockIdx.x;
@@ -177,8 +181,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     const int chunk = (slot % C::CHUNKS) ^ C::swz(key);
     goff[j] = uint32_t(key) * rs_bytes + uint32_t(chunk) * 16u;
   }
-  // lds_off: byte offset of the destination tile (any group's buffer).
-  auto fill = [&](const __bf16* base, int t, int lds_off) {
+  // dst: the destination tile array.
+  auto fill = [&](const __bf16* base, int t, char* dst) {
     const uint32_t off = uint32_t(t) * uint32_t(C::BN) * rs_bytes;
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(reinterpret_cast<const char*>(base)) + off, (short)0, int(valid_end - off),
@@ -186,14 +190,21 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 #pragma unroll
     for (int j = 0; j < C::SPT; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (lds_void*)(lds + lds_off + (gw * C::SPT + j) * 1024), 16, goff[j], 0, 0, 0);
+          rsrc, (lds_void*)(dst + (gw * C::SPT + j) * 1024), 16, goff[j], 0, 0, 0);
   };
-  auto k_off_of = [&](int g, int buf) { return C::K_OFF + (g * 2 + buf) * C::TILE; };
-  auto v_off_of = [&](int g, int buf) { return C::V_OFF + (g * 2 + buf) * C::TILE; };
-  auto k_off = [&](int buf) { return k_off_of(grp, buf); };
-  auto v_off = [&](int buf) { return v_off_of(grp, buf); };
+  // Tile arrays of key group G, buffer B (both compile-time).
+  auto ktile = [&](auto g, auto bf) -> char* {
+    constexpr int G = decltype(g)::value, B = decltype(bf)::value;
+    return G == 0 ? (B == 0 ? k00 : k01) : (B == 0 ? k10 : k11);
+  };
+  auto vtile = [&](auto g, auto bf) -> char* {
+    constexpr int G = decltype(g)::value, B = decltype(bf)::value;
+    return G == 0 ? (B == 0 ? v00 : v01) : (B == 0 ? v10 : v11);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
   const int n_g1 = n_tiles / 2;   // tiles of group 1 (local tile i is global tile 2i + 1)
-  float* bias_row = reinterpret_cast<float*>(lds + C::BIAS_OFF) + grp * 2 * C::BN;
+  float* bias_row = bias_all + grp * 2 * C::BN;
 
   // Key validity of tile t as an additive bias, one key per thread of wave 0.
   // The mask byte is loaded here and only compared when the bias row is
@@ -228,8 +239,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   const int vaddr0 = vaddr_of(0), vaddr1 = vaddr_of(1);
 
   // S^T[key][query] of one tile (two 32-key blocks).
-  auto qk = [&](int buf, f32x16* s) {
-    const char* kt = lds + k_off(buf);
+  auto qk = [&](const char* kt, f32x16* s) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 acc = f32x16{};
@@ -286,8 +296,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc_o[db] = f32x16{};
   // O^T[d][query] += V^T[d][keys] P^T[keys][query]
-  auto pv = [&](int buf, const bf16x8* pf) {
-    const char* vt = lds + v_off(buf);
+  auto pv = [&](const char* vt, const bf16x8* pf) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -319,11 +328,11 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       m_run = m_new;
     }
   };
-  auto prob_pv = [&](int vbuf) {
+  auto prob_pv = [&](const char* vt) {
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     bf16x8 pf[4];
     const float lsum = softmax(sc, m_use, pf);
-    pv(vbuf, pf);
+    pv(vt, pf);
     l_run += lsum;
   };
 
@@ -334,14 +343,14 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // the one on the critical path.
   if (grp == 0) {
     if (n_g > 0) {
-      fill(kbase, 2 * 0 + 0, k_off_of(0, 0));
-      fill(vbase, 2 * 0 + 0, v_off_of(0, 0));
+      fill(kbase, 2 * 0 + 0, ktile(I0{}, I0{}));
+      fill(vbase, 2 * 0 + 0, vtile(I0{}, I0{}));
     }
     if (n_g1 > 0) {
-      fill(kbase, 2 * 0 + 1, k_off_of(1, 0));
-      fill(vbase, 2 * 0 + 1, v_off_of(1, 0));
+      fill(kbase, 2 * 0 + 1, ktile(I1{}, I0{}));
+      fill(vbase, 2 * 0 + 1, vtile(I1{}, I0{}));
     }
-    if (n_g1 > 1) fill(kbase, 2 * 1 + 1, k_off_of(1, 1));
+    if (n_g1 > 1) fill(kbase, 2 * 1 + 1, ktile(I1{}, I1{}));
   }
   if (n_g > 0) {
     bias_of(tile_of(0));
@@ -358,65 +367,82 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // On each SIMD one wave of each group runs; right after every barrier group 0
   // is in its Q K^T MFMAs while group 1 is in its softmax VALU work, then the
   // roles swap, so the matrix pipe and the VALU overlap across the two waves.
+  // Iterations come in pairs so that every buffer choice is compile-time.
   if (grp == 0) {
-    for (int i = 0; i < n_iter; ++i) {
+    auto iter0 = [&](auto par, int i) {
+      constexpr int P = decltype(par)::value;
+      using BP = std::integral_constant<int, P>;
+      using BQ = std::integral_constant<int, 1 - P>;
       if (i < n_g) {
         const bool nx = i + 1 < n_g;
         if (nx) {
-          fill(kbase, 2 * (i + 1), k_off_of(0, (i + 1) & 1));
-          fill(vbase, 2 * (i + 1), v_off_of(0, (i + 1) & 1));
+          fill(kbase, 2 * (i + 1), ktile(I0{}, BQ{}));
+          fill(vbase, 2 * (i + 1), vtile(I0{}, BQ{}));
           bias_of(tile_of(i + 1));
         }
         // group 1's next K (two tiles ahead) and V (one tile ahead)
-        if (i + 2 < n_g1) fill(kbase, 2 * (i + 2) + 1, k_off_of(1, i & 1));
-        if (i + 1 < n_g1) fill(vbase, 2 * (i + 1) + 1, v_off_of(1, (i + 1) & 1));
+        if (i + 2 < n_g1) fill(kbase, 2 * (i + 2) + 1, ktile(I1{}, BP{}));
+        if (i + 1 < n_g1) fill(vbase, 2 * (i + 1) + 1, vtile(I1{}, BQ{}));
         __builtin_amdgcn_sched_barrier(0);
-        qk(i & 1, sc);
-        rescale(bias_max(i & 1, tile_of(i), sc));
-        prob_pv(i & 1);
-        if (nx) store_bias((i + 1) & 1);
+        qk(ktile(I0{}, BP{}), sc);
+        rescale(bias_max(P, tile_of(i), sc));
+        prob_pv(vtile(I0{}, BP{}));
+        if (nx) store_bias(1 - P);
       }
       __builtin_amdgcn_s_waitcnt(0x0f70);
       __syncthreads();
+    };
+    for (int i = 0; i < n_iter; i += 2) {
+      iter0(I0{}, i);
+      if (i + 1 < n_iter) iter0(I1{}, i + 1);
     }
   } else {
     if (n_g > 0) {
-      qk(0, sc);
+      qk(ktile(I1{}, I0{}), sc);
       m_run = bias_max(0, tile_of(0), sc);
     }
-    for (int i = 0; i < n_iter; ++i) {
+    auto iter1 = [&](auto par, int i) {
+      constexpr int P = decltype(par)::value;
+      using BP = std::integral_constant<int, P>;
+      using BQ = std::integral_constant<int, 1 - P>;
       if (i < n_g) {
         const bool nx = i + 1 < n_g, nk = i + 2 < n_g;
         if (nk) bias_of(tile_of(i + 2));
         __builtin_amdgcn_sched_barrier(0);
-        prob_pv(i & 1);
+        prob_pv(vtile(I1{}, BP{}));
         __builtin_amdgcn_sched_barrier(0);
         if (nx) {
-          qk((i + 1) & 1, sc);
-          rescale(bias_max((i + 1) & 1, tile_of(i + 1), sc));
+          qk(ktile(I1{}, BQ{}), sc);
+          rescale(bias_max(1 - P, tile_of(i + 1), sc));
         }
-        if (nk) store_bias(i & 1);
+        if (nk) store_bias(P);
       }
       __builtin_amdgcn_s_waitcnt(0x0f70);
       __syncthreads();
+    };
+    for (int i = 0; i < n_iter; i += 2) {
+      iter1(I0{}, i);
+      if (i + 1 < n_iter) iter1(I1{}, i + 1);
     }
   }
 
-  // ---- merge the two groups' softmax states through LDS (reusing the tiles)
-  float* comb = reinterpret_cast<float*>(lds);
-  auto slot = [&](int k) { return (gw * C::NCOMB + k) * 64 + lane; };
+  // ---- merge the two groups' softmax states through LDS (reusing the K tile
+  // arrays: O of group-1 wave gw in one array each, m and l in the first V array)
+  float* comb = reinterpret_cast<float*>(gw == 0 ? k00 : gw == 1 ? k01 : gw == 2 ? k10 : k11);
+  float* comb_ml = reinterpret_cast<float*>(v00) + gw * 2 * 64;
+  auto slot = [&](int k) { return k * 64 + lane; };
   if (grp == 1) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) comb[slot(db * 16 + r)] = acc_o[db][r];
-    comb[slot(C::DB * 16)] = m_run;
-    comb[slot(C::DB * 16 + 1)] = l_run;
+    comb_ml[slot(0)] = m_run;
+    comb_ml[slot(1)] = l_run;
   }
   __syncthreads();
   if (grp == 0) {
-    const float m1 = comb[slot(C::DB * 16)];
-    const float l1 = comb[slot(C::DB * 16 + 1)];
+    const float m1 = comb_ml[slot(0)];
+    const float l1 = comb_ml[slot(1)];
     const float mm = fmaxf(m_run, m1);
     const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
     const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);

@@ -28,6 +28,10 @@ SIGNATURES = {
                                                _i64, ctypes.c_float, ctypes.c_int, _vp]),
     "cp_output_reverse": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                          ctypes.c_int, _vp]),
+    "cp_attn_localq_globalkv_ws": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                                  _i64, ctypes.c_float, ctypes.c_int, _vp,
+                                                  ctypes.c_size_t, _vp]),
+    "cp_attn_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64]),
 }
 
 # Status codes (enum cp_status).
@@ -42,10 +46,11 @@ CP_ERR_ALIAS = 7
 CP_ERR_SCALE = 8
 CP_ERR_UNSUPPORTED = 9
 CP_ERR_HIP = 10
+CP_ERR_WORKSPACE = 11
 
 CP_DTYPE_BF16 = 0
 CP_DTYPE_FP16 = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _lib = None
 

@@ -46,6 +46,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 #include <utility>
@@ -106,8 +107,14 @@ struct AttnArgs {
   __bf16* o;
   int B, Sq, Skv, H;
   int m_tiles;  // ceil(Sq / BM)
-  int n_work;   // B * H * m_tiles
+  int n_work;   // B * H * m_tiles  (query blocks)
   float sc;     // scale * log2(e)
+  // Split-KV: with nsplit > 1, workgroup w takes part j = w % nsplit of the key
+  // iterations of query block w / nsplit, [n_iter * j / nsplit, n_iter * (j + 1) / nsplit),
+  // and writes its partial state to workspace slot w.
+  int nsplit;          // 1: one workgroup per query block
+  int n_iter_blk;      // iterations per query block: ceil(ceil(Skv / BN) / 2)
+  float* ws;           // partial states: [n_work * nsplit][BM][D + 2] (O, m, l per row)
 };
 
 // The body is a device function behind a thin kernel: the LDS address-space
@@ -123,17 +130,6 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   __shared__ __attribute__((aligned(1024))) char v00[C::TILE], v01[C::TILE], v10[C::TILE], v11[C::TILE];
   __shared__ __attribute__((aligned(16))) float bias_all[kGroups * 2 * C::BN];
 
-  // ---- XCD-aware work numbering: consecutive logical tiles share an XCD.
-  const int pid = blockIdx.x;
-  const int n = a.n_work;
-  const int per = n / kNumXcd, rem = n % kNumXcd;
-  const int xcd = pid % kNumXcd, local = pid / kNumXcd;
-  const int work = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-  const int mt = work % a.m_tiles;
-  const int bh = work / a.m_tiles;
-  const int h = bh % a.H;
-  const int b = bh / a.H;
-
   const int tid = threadIdx.x;
   // Wave-uniform indices go through readfirstlane so that the compiler keeps
   // them (and the buffer descriptors and LDS bases built from them) scalar.
@@ -144,6 +140,14 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;  // half of the wave: selects the 8-wide k slice of an MFMA operand
 
+  // One segment: query block `work`, iterations [i0, i1) of it.  slot_idx < 0:
+  // the segment is the whole block and writes O; otherwise it writes its
+  // partial state to workspace slot slot_idx.
+  auto process = [&](int work, int i0, int i1, int slot_idx) {
+  const int mt = work % a.m_tiles;
+  const int bh = work / a.m_tiles;
+  const int h = bh % a.H;
+  const int b = bh / a.H;
   const size_t row_stride = size_t(a.H) * D;  // elements between consecutive sequence rows
   const __bf16* kbase = a.k + (size_t(b) * a.Skv * a.H + h) * D;
   const __bf16* vbase = a.v + (size_t(b) * a.Skv * a.H + h) * D;
@@ -164,9 +168,11 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   }
 
   const int n_tiles = (a.Skv + C::BN - 1) / C::BN;
-  const int n_iter = (n_tiles + 1) / 2;     // iterations of every wave
-  const int n_g = (n_tiles - grp + 1) / 2;  // tiles of this group
-  auto tile_of = [&](int i) { return 2 * i + grp; };
+  const int n_iter = i1 - i0;  // iterations of every wave in this segment
+  // tiles of key group g in the segment: global tiles 2 (i0 + j) + g < n_tiles
+  auto tiles_of_group = [&](int g) { return min(n_iter, max(0, (n_tiles - g + 1) / 2 - i0)); };
+  const int n_g = tiles_of_group(grp);
+  auto tile_of = [&](int i) { return 2 * (i0 + i) + grp; };
 
   // ---- HBM -> LDS fill.  Slot s of a tile (16 bytes) holds chunk
   // (s % CHUNKS) ^ swz(key) of row key = s / CHUNKS; instruction j of wave gw
@@ -203,7 +209,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  const int n_g1 = n_tiles / 2;   // tiles of group 1 (local tile i is global tile 2i + 1)
+  const int n_g1 = tiles_of_group(1);  // tiles of group 1 (local tile i is global tile 2(i0 + i) + 1)
   float* bias_row = bias_all + grp * 2 * C::BN;
 
   // Key validity of tile t as an additive bias, one key per thread of wave 0.
@@ -343,14 +349,14 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // the one on the critical path.
   if (grp == 0) {
     if (n_g > 0) {
-      fill(kbase, 2 * 0 + 0, ktile(I0{}, I0{}));
-      fill(vbase, 2 * 0 + 0, vtile(I0{}, I0{}));
+      fill(kbase, 2 * (i0 + 0) + 0, ktile(I0{}, I0{}));
+      fill(vbase, 2 * (i0 + 0) + 0, vtile(I0{}, I0{}));
     }
     if (n_g1 > 0) {
-      fill(kbase, 2 * 0 + 1, ktile(I1{}, I0{}));
-      fill(vbase, 2 * 0 + 1, vtile(I1{}, I0{}));
+      fill(kbase, 2 * (i0 + 0) + 1, ktile(I1{}, I0{}));
+      fill(vbase, 2 * (i0 + 0) + 1, vtile(I1{}, I0{}));
     }
-    if (n_g1 > 1) fill(kbase, 2 * 1 + 1, ktile(I1{}, I1{}));
+    if (n_g1 > 1) fill(kbase, 2 * (i0 + 1) + 1, ktile(I1{}, I1{}));
   }
   if (n_g > 0) {
     bias_of(tile_of(0));
@@ -376,13 +382,13 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       if (i < n_g) {
         const bool nx = i + 1 < n_g;
         if (nx) {
-          fill(kbase, 2 * (i + 1), ktile(I0{}, BQ{}));
-          fill(vbase, 2 * (i + 1), vtile(I0{}, BQ{}));
+          fill(kbase, 2 * (i0 + i + 1), ktile(I0{}, BQ{}));
+          fill(vbase, 2 * (i0 + i + 1), vtile(I0{}, BQ{}));
           bias_of(tile_of(i + 1));
         }
         // group 1's next K (two tiles ahead) and V (one tile ahead)
-        if (i + 2 < n_g1) fill(kbase, 2 * (i + 2) + 1, ktile(I1{}, BP{}));
-        if (i + 1 < n_g1) fill(vbase, 2 * (i + 1) + 1, vtile(I1{}, BQ{}));
+        if (i + 2 < n_g1) fill(kbase, 2 * (i0 + i + 2) + 1, ktile(I1{}, BP{}));
+        if (i + 1 < n_g1) fill(vbase, 2 * (i0 + i + 1) + 1, vtile(I1{}, BQ{}));
         __builtin_amdgcn_sched_barrier(0);
         qk(ktile(I0{}, BP{}), sc);
         rescale(bias_max(P, tile_of(i), sc));
@@ -447,6 +453,26 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
     const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
     const float l_tot = pair_sum(a0 * l_run + a1 * l1);
+    if (slot_idx >= 0) {
+      // partial state of this segment: unnormalized O (relative to mm), mm, l
+      float* wp = a.ws + (size_t(slot_idx) * C::BM + gw * 32 + l32) * (D + 2);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float4 w;
+          w.x = acc_o[db][4 * g + 0] * a0 + comb[slot(db * 16 + 4 * g + 0)] * a1;
+          w.y = acc_o[db][4 * g + 1] * a0 + comb[slot(db * 16 + 4 * g + 1)] * a1;
+          w.z = acc_o[db][4 * g + 2] * a0 + comb[slot(db * 16 + 4 * g + 2)] * a1;
+          w.w = acc_o[db][4 * g + 3] * a0 + comb[slot(db * 16 + 4 * g + 3)] * a1;
+          *reinterpret_cast<float4*>(wp + db * 32 + 8 * g + 4 * hi) = w;
+        }
+      if (hi == 0) {
+        wp[D] = mm;
+        wp[D + 1] = l_tot;
+      }
+      return;
+    }
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const float c0 = a0 * inv, c1 = a1 * inv;
     if (q_row < a.Sq) {
@@ -466,6 +492,68 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
         }
     }
   }
+  };  // process
+
+  const int n_iter_blk = a.n_iter_blk;
+  // XCD-aware numbering: consecutive logical indices (query blocks, or the
+  // parts of one block) run on one XCD and its L2.
+  const int pid = blockIdx.x;
+  const int n = a.n_work * a.nsplit;
+  const int per = n / kNumXcd, rem = n % kNumXcd;
+  const int xcd = pid % kNumXcd, local = pid / kNumXcd;
+  const int logical = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  if (a.nsplit == 1) {
+    process(logical, 0, n_iter_blk, -1);
+  } else {
+    const int j = logical % a.nsplit;
+    process(logical / a.nsplit, n_iter_blk * j / a.nsplit, n_iter_blk * (j + 1) / a.nsplit, logical);
+  }
+}
+
+// Merges the nsplit partial states of each query block:
+// O = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k per row, M = max_k m_k (0 when
+// no key of the row is valid).  One workgroup per query block, two threads
+// per row.
+template <int D>
+__global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
+  constexpr int BM = Cfg<D>::BM;
+  const int blk = blockIdx.x;
+  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int mt = blk % a.m_tiles, bh = blk / a.m_tiles, h = bh % a.H, b = bh / a.H;
+  const int q_row = mt * BM + row;
+  if (q_row >= a.Sq) return;
+  auto part = [&](int j) { return a.ws + (size_t(blk * a.nsplit + j) * BM + row) * (D + 2); };
+  float M = -INFINITY;
+  for (int j = 0; j < a.nsplit; ++j) M = fmaxf(M, part(j)[D]);
+  float acc[D / 2];
+#pragma unroll
+  for (int d = 0; d < D / 2; ++d) acc[d] = 0.f;
+  float L = 0.f;
+  for (int j = 0; j < a.nsplit; ++j) {
+    const float* wp = part(j);
+    const float mk = wp[D];
+    const float f = mk == -INFINITY ? 0.f : exp2f(mk - M);
+    L += f * wp[D + 1];
+#pragma unroll
+    for (int d = 0; d < D / 2; d += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(wp + half * (D / 2) + d);
+      acc[d] += f * x.x;
+      acc[d + 1] += f * x.y;
+      acc[d + 2] += f * x.z;
+      acc[d + 3] += f * x.w;
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  __bf16* op = a.o + (size_t(b) * a.Sq + q_row) * (size_t(a.H) * D) + size_t(h) * D + half * (D / 2);
+#pragma unroll
+  for (int d = 0; d < D / 2; d += 4) {
+    bf16x4 w;
+    w[0] = (__bf16)(acc[d] * inv);
+    w[1] = (__bf16)(acc[d + 1] * inv);
+    w[2] = (__bf16)(acc[d + 2] * inv);
+    w[3] = (__bf16)(acc[d + 3] * inv);
+    *reinterpret_cast<bf16x4*>(op + d) = w;
+  }
 }
 
 template <int D>
@@ -478,16 +566,19 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(AttnArgs a) {
 
 using namespace cpattn;
 
-extern "C" int cp_attn_localq_globalkv(const void* q, const void* k, const void* v,
-                                       const uint8_t* key_mask, void* o, int64_t B, int64_t Sq,
-                                       int64_t Skv, int64_t H, int64_t D, float scale,
-                                       int causal, cp_stream_t stream) {
+namespace {
+
+// Validation, plan and launch shared by both entry points.
+int attn_run(const void* q, const void* k, const void* v, const uint8_t* key_mask, void* o, int64_t B,
+             int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale, int causal, void* ws, size_t ws_bytes,
+             cp_stream_t stream) {
   if (!q || !k || !v || !o) return CP_ERR_NULL;
   if (B < 1 || Sq < 1 || Skv < 1 || H < 1) return CP_ERR_SHAPE;
   if (D != 64 && D != 128) return CP_ERR_HEAD_DIM;
   if (!std::isfinite(scale) || !(scale > 0.f)) return CP_ERR_SCALE;
   if (causal != 0) return CP_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return CP_ERR_ALIGNMENT;
+  if (ws && !aligned16(ws)) return CP_ERR_ALIGNMENT;
   // Per-dimension sizes and the work count are kept in int on the device.
   constexpr int64_t kIntMax = 0x7fffffff;
   if (B > kIntMax || Sq > kIntMax || Skv > kIntMax - 64 || H > kIntMax) return CP_ERR_SHAPE;
@@ -516,10 +607,58 @@ extern "C" int cp_attn_localq_globalkv(const void* q, const void* k, const void*
   args.m_tiles = int(m_tiles);
   args.n_work = int(n_work);
   args.sc = scale * 1.4426950408889634f;
+  const int64_t n_tiles = (Skv + 63) / 64;
+  args.n_iter_blk = int((n_tiles + 1) / 2);
+  args.nsplit = 1;
+  args.ws = nullptr;
+  // Split the key range of every query block into nsplit parts when the query
+  // blocks alone would occupy at most half of the compute units; each part
+  // keeps at least kMinSplitIters iterations.
+  constexpr int64_t kMinSplitIters = 4;
+  if (ws) {
+    const int64_t cus = num_cus();
+    const int64_t nsplit = std::min<int64_t>(cus / n_work, args.n_iter_blk / kMinSplitIters);
+    if (2 * n_work <= cus && nsplit >= 2) {
+      const size_t need = size_t(n_work * nsplit) * size_t(bm) * size_t(D + 2) * sizeof(float);
+      if (ws_bytes < need) return CP_ERR_WORKSPACE;
+      if (overlaps(ws, need, q, qb) || overlaps(ws, need, k, kb) || overlaps(ws, need, v, kb) ||
+          overlaps(ws, need, o, qb) || (key_mask && overlaps(ws, need, key_mask, size_t(B * Skv))))
+        return CP_ERR_ALIAS;
+      args.nsplit = int(nsplit);
+      args.ws = static_cast<float*>(ws);
+    }
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (D == 128)
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(unsigned(n_work)), dim3(kThreads), 0, s, args);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(unsigned(n_work)), dim3(kThreads), 0, s, args);
+  const dim3 grid{unsigned(n_work * args.nsplit)}, block{unsigned(kThreads)}, cblock{256u}, cgrid{unsigned(n_work)};
+  if (D == 128) {
+    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, block, 0, s, args);
+    if (args.nsplit > 1) hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, cblock, 0, s, args);
+  } else {
+    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, block, 0, s, args);
+    if (args.nsplit > 1) hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, cblock, 0, s, args);
+  }
   return hip_status(hipGetLastError());
+}
+
+}  // namespace
+
+extern "C" int cp_attn_localq_globalkv(const void* q, const void* k, const void* v,
+                                       const uint8_t* key_mask, void* o, int64_t B, int64_t Sq,
+                                       int64_t Skv, int64_t H, int64_t D, float scale,
+                                       int causal, cp_stream_t stream) {
+  return attn_run(q, k, v, key_mask, o, B, Sq, Skv, H, D, scale, causal, nullptr, 0, stream);
+}
+
+extern "C" int cp_attn_localq_globalkv_ws(const void* q, const void* k, const void* v,
+                                          const uint8_t* key_mask, void* o, int64_t B, int64_t Sq,
+                                          int64_t Skv, int64_t H, int64_t D, float scale, int causal,
+                                          void* workspace, size_t workspace_bytes, cp_stream_t stream) {
+  return attn_run(q, k, v, key_mask, o, B, Sq, Skv, H, D, scale, causal, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t cp_attn_workspace_bytes(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D) {
+  if (D != 64 && D != 128) return 0;
+  if (B < 1 || Sq < 1 || Skv < 1 || H < 1) return 0;
+  // at most one partial slot of BM x (D + 2) floats per compute unit
+  return size_t(num_cus()) * size_t(32 * kGroupWaves) * size_t(D + 2) * sizeof(float);
 }

@@ -36,6 +36,19 @@ constexpr int64_t kMaxVectors = (int64_t(1) << 31) - 1;
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? CP_OK : CP_ERR_HIP; }
 
+// Compute units of the current device (cached per device; 256 if unknown).
+inline int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // ---------------------------------------------------------------- fast division
 // Division of n < 2^31 by a runtime divisor d in [1, 2^31): q = (umulhi(n, m) + n) >> s
 // with s = ceil(log2 d) and m = floor(2^32 * (2^s - d) / d) + 1 (Granlund and

@@ -175,18 +175,6 @@ struct ExchangeMap {
   __device__ __forceinline__ vec_t* dst(uint32_t o) const { return recv + o; }
 };
 
-int num_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 inline unsigned grid_for(uint32_t n_vec) {
   const unsigned tiles = (n_vec + kVecPerBlock - 1) / kVecPerBlock;
   const unsigned cap = unsigned(num_cus()) * kBlocksPerCu;

@@ -131,8 +131,15 @@ def cp_unpack_head_sharded(recv, B: int, W: int, out=None, stream=None):
 
 
 def cp_attn_localq_globalkv(q, k, v, key_mask=None, scale=None, out=None, causal=False,
-                            stream=None) -> torch.Tensor:
-    """Non-causal attention: q [B,Sq,H,D] vs k, v [B,Skv,H,D] (bf16), optional uint8 mask [B,Skv]."""
+                            stream=None, split=True, workspace=None) -> torch.Tensor:
+    """Non-causal attention: q [B,Sq,H,D] vs k, v [B,Skv,H,D] (bf16), optional uint8 mask [B,Skv].
+
+    split=True lets the library split the key range of query blocks over
+    workgroups when the problem has too few query blocks to fill the GPU; the
+    workspace (a uint8 tensor of at least cp_attn_workspace_bytes bytes) comes
+    from the staging cache unless given.  split=False uses the entry point
+    without a workspace (one workgroup per query block).
+    """
     lib = _lib.load()
     B, Sq, H, D = q.shape
     Skv = k.shape[1]
@@ -151,10 +158,26 @@ def cp_attn_localq_globalkv(q, k, v, key_mask=None, scale=None, out=None, causal
         out = torch.empty_like(q)
     if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q")
-    _lib.check("cp_attn_localq_globalkv", lib.cp_attn_localq_globalkv(
+    if not split:
+        _lib.check("cp_attn_localq_globalkv", lib.cp_attn_localq_globalkv(
+            _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), mask_ptr, _dev(out, "o"),
+            B, Sq, Skv, H, D, float(scale), int(bool(causal)), _stream(stream)))
+        return out
+    need = int(lib.cp_attn_workspace_bytes(B, Sq, Skv, H, D))
+    if workspace is None:
+        workspace = staging_buffer("attn_workspace", (max(need, 16),), torch.uint8, q.device)
+    elif workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+    _lib.check("cp_attn_localq_globalkv_ws", lib.cp_attn_localq_globalkv_ws(
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), mask_ptr, _dev(out, "o"),
-        B, Sq, Skv, H, D, float(scale), int(bool(causal)), _stream(stream)))
+        B, Sq, Skv, H, D, float(scale), int(bool(causal)), _dev(workspace, "workspace"),
+        workspace.numel(), _stream(stream)))
     return out
+
+
+def cp_attn_workspace_bytes(B: int, Sq: int, Skv: int, H: int, D: int) -> int:
+    """Workspace bytes cp_attn_localq_globalkv may use with split=True (upper bound, current device)."""
+    return int(_lib.load().cp_attn_workspace_bytes(B, Sq, Skv, H, D))
 
 
 def cp_output_reverse(phase: int, src, W: int, B: int, out=None, stream=None) -> torch.Tensor:

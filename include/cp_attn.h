@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CP_ABI_VERSION 1
+#define CP_ABI_VERSION 2
 
 typedef struct ihipStream_t* cp_stream_t; /* == hipStream_t */
 
@@ -69,7 +69,8 @@ enum cp_status {
   CP_ERR_ALIAS = 7,        /* an output overlaps an input or another output */
   CP_ERR_SCALE = 8,        /* softmax scale is not finite or not > 0 */
   CP_ERR_UNSUPPORTED = 9,  /* a valid but unsupported request (causal, bad phase, W too large) */
-  CP_ERR_HIP = 10          /* the HIP runtime rejected the launch */
+  CP_ERR_HIP = 10,         /* the HIP runtime rejected the launch */
+  CP_ERR_WORKSPACE = 11    /* the workspace is too small (see cp_attn_workspace_bytes) */
 };
 
 enum cp_dtype { CP_DTYPE_BF16 = 0, CP_DTYPE_FP16 = 1 };
@@ -153,6 +154,39 @@ int cp_attn_localq_globalkv(const void* q, const void* k, const void* v,
                             const uint8_t* key_mask, void* o,
                             int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D,
                             float scale, int causal, cp_stream_t stream);
+
+/*
+ * The same attention with a caller-owned workspace, which lets the library
+ * split the key range of each query block (128 query rows) over several
+ * workgroups, with the partial softmax states merged by their log-sum-exp as
+ * split-KV / FlashDecoding do, when the query blocks alone would occupy at
+ * most half of the GPU.  The
+ * [vllm-omni#7641] "Recommended follow-up" note on attention over arriving
+ * K/V chunks is the same merge.  The split is deterministic for a given
+ * problem and device, so results are reproducible run to run.
+ *
+ *   workspace       : NULL (never split; identical to cp_attn_localq_globalkv),
+ *                     or device memory of workspace_bytes, 16-byte aligned,
+ *                     disjoint from q, k, v, o and key_mask.  Contents on
+ *                     entry are ignored; the library never allocates.
+ *   workspace_bytes : at least cp_attn_workspace_bytes(B, Sq, Skv, H, D)
+ *                     for the current device, else CP_ERR_WORKSPACE.
+ *
+ * The workspace is used by the kernels enqueued on `stream`; reusing it on
+ * another stream without ordering is a race.
+ */
+int cp_attn_localq_globalkv_ws(const void* q, const void* k, const void* v,
+                               const uint8_t* key_mask, void* o,
+                               int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D,
+                               float scale, int causal, void* workspace, size_t workspace_bytes,
+                               cp_stream_t stream);
+
+/*
+ * Bytes of workspace cp_attn_localq_globalkv_ws may use for this problem on
+ * the current device (an upper bound: one partial slot of 128 x (D + 2) floats
+ * per compute unit).  0 for an unsupported D.  No GPU work, no allocation.
+ */
+size_t cp_attn_workspace_bytes(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D);
 
 /*
  * Ulysses output exchange ([sglang#33667] names _usp_output_all_to_all in its

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings():
     lib = _lib.load()
     seen = set()
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = lib.cp_status_string(code).decode()
         assert s and s not in seen
         seen.add(s)
@@ -86,6 +86,15 @@ def _attn(**kw):
     return _lib.load().cp_attn_localq_globalkv(a["q"], a["k"], a["v"], a["m"], a["o"], a["B"],
                                                a["Sq"], a["Skv"], a["H"], a["D"], a["scale"],
                                                a["causal"], None)
+
+
+def _attn_ws(**kw):
+    a = dict(q=A, k=A + BIG, v=A + 2 * BIG, m=None, o=A + 3 * BIG, B=1, Sq=8, Skv=16, H=2,
+             D=128, scale=0.125, causal=0, ws=A + 5 * BIG, nbytes=16)
+    a.update(kw)
+    return _lib.load().cp_attn_localq_globalkv_ws(a["q"], a["k"], a["v"], a["m"], a["o"], a["B"],
+                                                  a["Sq"], a["Skv"], a["H"], a["D"], a["scale"],
+                                                  a["causal"], a["ws"], a["nbytes"], None)
 
 
 def _rev(**kw):
@@ -158,6 +167,28 @@ def test_unpack_rejects(kw, code):
 ])
 def test_attention_rejects(kw, code):
     assert _attn(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(Skv=4096), _lib.CP_ERR_WORKSPACE),          # 2 query blocks x 32 iterations split; 16 bytes is too small
+    (dict(ws=A + 5 * BIG + 8), _lib.CP_ERR_ALIGNMENT),
+    (dict(Skv=4096, ws=A + 3 * BIG, nbytes=1 << 30), _lib.CP_ERR_ALIAS),   # workspace overlaps o
+    (dict(o=None), _lib.CP_ERR_NULL),
+    (dict(D=96), _lib.CP_ERR_HEAD_DIM),
+    (dict(causal=1), _lib.CP_ERR_UNSUPPORTED),
+])
+def test_attention_ws_rejects(kw, code):
+    assert _attn_ws(**kw) == code
+
+
+def test_workspace_bytes():
+    lib = _lib.load()
+    n = lib.cp_attn_workspace_bytes(1, 1088, 4352, 24, 128)
+    # one partial slot of 128 rows x (128 + 2) floats per compute unit
+    assert n > 0 and n % (128 * 130 * 4) == 0
+    assert lib.cp_attn_workspace_bytes(1, 1088, 4352, 24, 96) == 0
+    assert lib.cp_attn_workspace_bytes(0, 1088, 4352, 24, 128) == 0
 
 
 @cpu_only

@@ -170,3 +170,41 @@ def test_full_size_workloads_sampled(gu, name):
         vv = vf[b][valid]
         lo, hi = vv.min(dim=0).values.numpy(), vv.max(dim=0).values.numpy()
         assert (got[b] >= lo - 1e-2).all() and (got[b] <= hi + 1e-2).all()
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,D,masked", [
+    (1, 2, 130, 4096, 128, False),   # 4 query blocks x 32 iterations: every block split over 32 workgroups
+    (2, 3, 70, 700, 64, True),       # masked, ragged keys, D 64
+    (1, 1, 5, 3000, 128, True),      # one query block split many ways, most rows invalid
+    (1, 24, 1088, 4352, 128, False),  # image CP4 share: 216 blocks, split over the compute units
+])
+def test_split_kv_matches_oracle_and_unsplit(gu, B, H, Sq, Skv, D, masked):
+    import context_attention_diffusion_amd as cp
+    seed = 9000 + Sq + Skv + D
+    q = _rand_bits((B, Sq, H, D), seed)
+    k = _rand_bits((B, Skv, H, D), seed + 1)
+    v = _rand_bits((B, Skv, H, D), seed + 2)
+    mask = None
+    if masked:
+        mask = (np.random.default_rng(seed + 3).random((B, Skv)) > 0.4).astype(np.uint8)
+        mask[:, 0] = 1
+    qd, kd, vd = gu.to_dev(q), gu.to_dev(k), gu.to_dev(v)
+    md = None if mask is None else torch.from_numpy(mask).to(gu.DEV)
+    print(f"[attn] split B={B} H={H} Sq={Sq} Skv={Skv} D={D} masked={masked}", flush=True)
+    o_split = cp.cp_attn_localq_globalkv(qd, kd, vd, md, split=True)
+    o_split2 = cp.cp_attn_localq_globalkv(qd, kd, vd, md, split=True)
+    o_whole = cp.cp_attn_localq_globalkv(qd, kd, vd, md, split=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o_split, o_split2), "split results differ between runs"
+    got, whole = gu.to_f64(o_split), gu.to_f64(o_whole)
+    if Sq * Skv * H * B <= 4_000_000:
+        ref = OA.attention(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), mask)
+        _assert_close(got, ref, f"split B{B} H{H} Sq{Sq} Skv{Skv} D{D} m{int(masked)}")
+    else:  # sampled rows at full size
+        rng = np.random.default_rng(seed)
+        rows = [(int(rng.integers(B)), int(rng.integers(Sq)), int(rng.integers(H))) for _ in range(48)]
+        ref = OA.attention_rows(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), rows, mask)
+        sel = np.stack([got[b_, i_, h_] for b_, i_, h_ in rows])
+        _assert_close(sel, ref, f"split sampled B{B} H{H} Sq{Sq} Skv{Skv}")
+    # the two schedules sum the same terms in a different order
+    assert np.abs(got - whole).max() <= 2e-2

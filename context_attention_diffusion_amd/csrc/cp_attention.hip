@@ -114,7 +114,8 @@ struct AttnArgs {
   // and writes its partial state to workspace slot w.
   int nsplit;          // 1: one workgroup per query block
   int n_iter_blk;      // iterations per query block: ceil(ceil(Skv / BN) / 2)
-  float* ws;           // partial states: [n_work * nsplit][BM][D + 2] (O, m, l per row)
+  float* ws;           // partial states, slot = query block * nsplit + part:
+                       // O [n_work * nsplit][BM][D] fp32, then (m, l) [n_work * nsplit][BM][2]
 };
 
 // The body is a device function behind a thin kernel: the LDS address-space
@@ -455,7 +456,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     const float l_tot = pair_sum(a0 * l_run + a1 * l1);
     if (slot_idx >= 0) {
       // partial state of this segment: unnormalized O (relative to mm), mm, l
-      float* wp = a.ws + (size_t(slot_idx) * C::BM + gw * 32 + l32) * (D + 2);
+      const size_t prow = size_t(slot_idx) * C::BM + gw * 32 + l32;
+      float* wp = a.ws + prow * D;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -468,8 +470,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
           *reinterpret_cast<float4*>(wp + db * 32 + 8 * g + 4 * hi) = w;
         }
       if (hi == 0) {
-        wp[D] = mm;
-        wp[D + 1] = l_tot;
+        float* ml = a.ws + size_t(a.n_work) * a.nsplit * C::BM * D + prow * 2;
+        ml[0] = mm;
+        ml[1] = l_tot;
       }
       return;
     }
@@ -512,48 +515,44 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 
 // Merges the nsplit partial states of each query block:
 // O = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k per row, M = max_k m_k (0 when
-// no key of the row is valid).  One workgroup per query block, two threads
-// per row.
+// no key of the row is valid).  A thread owns four consecutive head-dim columns
+// of one row, so a wave reads whole rows of every partial O.
 template <int D>
 __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   constexpr int BM = Cfg<D>::BM;
-  const int blk = blockIdx.x;
-  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+  constexpr int TPR = D / 4;                 // threads per row
+  constexpr int RPW = 256 / TPR;             // rows per workgroup
+  constexpr int WPB = BM / RPW;              // workgroups per query block
+  const int blk = blockIdx.x / WPB;
+  const int row = (blockIdx.x % WPB) * RPW + threadIdx.x / TPR;
+  const int c4 = (threadIdx.x % TPR) * 4;
   const int mt = blk % a.m_tiles, bh = blk / a.m_tiles, h = bh % a.H, b = bh / a.H;
   const int q_row = mt * BM + row;
   if (q_row >= a.Sq) return;
-  auto part = [&](int j) { return a.ws + (size_t(blk * a.nsplit + j) * BM + row) * (D + 2); };
+  const size_t slot0 = size_t(blk) * a.nsplit;
+  const float* ml = a.ws + size_t(a.n_work) * a.nsplit * BM * D;
   float M = -INFINITY;
-  for (int j = 0; j < a.nsplit; ++j) M = fmaxf(M, part(j)[D]);
-  float acc[D / 2];
-#pragma unroll
-  for (int d = 0; d < D / 2; ++d) acc[d] = 0.f;
+  for (int j = 0; j < a.nsplit; ++j) M = fmaxf(M, ml[((slot0 + j) * BM + row) * 2]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float L = 0.f;
   for (int j = 0; j < a.nsplit; ++j) {
-    const float* wp = part(j);
-    const float mk = wp[D];
+    const size_t prow = (slot0 + j) * BM + row;
+    const float mk = ml[prow * 2], lk = ml[prow * 2 + 1];
     const float f = mk == -INFINITY ? 0.f : exp2f(mk - M);
-    L += f * wp[D + 1];
-#pragma unroll
-    for (int d = 0; d < D / 2; d += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(wp + half * (D / 2) + d);
-      acc[d] += f * x.x;
-      acc[d + 1] += f * x.y;
-      acc[d + 2] += f * x.z;
-      acc[d + 3] += f * x.w;
-    }
+    const float4 x = *reinterpret_cast<const float4*>(a.ws + prow * D + c4);
+    L += f * lk;
+    acc.x += f * x.x;
+    acc.y += f * x.y;
+    acc.z += f * x.z;
+    acc.w += f * x.w;
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  __bf16* op = a.o + (size_t(b) * a.Sq + q_row) * (size_t(a.H) * D) + size_t(h) * D + half * (D / 2);
-#pragma unroll
-  for (int d = 0; d < D / 2; d += 4) {
-    bf16x4 w;
-    w[0] = (__bf16)(acc[d] * inv);
-    w[1] = (__bf16)(acc[d + 1] * inv);
-    w[2] = (__bf16)(acc[d + 2] * inv);
-    w[3] = (__bf16)(acc[d + 3] * inv);
-    *reinterpret_cast<bf16x4*>(op + d) = w;
-  }
+  bf16x4 w;
+  w[0] = (__bf16)(acc.x * inv);
+  w[1] = (__bf16)(acc.y * inv);
+  w[2] = (__bf16)(acc.z * inv);
+  w[3] = (__bf16)(acc.w * inv);
+  *reinterpret_cast<bf16x4*>(a.o + (size_t(b) * a.Sq + q_row) * (size_t(a.H) * D) + size_t(h) * D + c4) = w;
 }
 
 template <int D>
@@ -629,7 +628,7 @@ int attn_run(const void* q, const void* k, const void* v, const uint8_t* key_mas
     }
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const dim3 grid{unsigned(n_work * args.nsplit)}, block{unsigned(kThreads)}, cblock{256u}, cgrid{unsigned(n_work)};
+  const dim3 grid{unsigned(n_work * args.nsplit)}, block{unsigned(kThreads)}, cblock{256u}, cgrid{unsigned(n_work * (D / 8))};  // BM * D / 4 threads of 256 per block
   if (D == 128) {
     hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, block, 0, s, args);
     if (args.nsplit > 1) hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, cblock, 0, s, args);

@@ -99,7 +99,29 @@ struct Cfg {
 __device__ __forceinline__ float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
 
+// Row addressing of one operand: element (b, i, h, d) of a [B][S][H][D] view
+// lies at  b * bs + row_off(i) + h * hs + d  elements from the base, with
+// row_off(i) = (i / L) * cs + (i % L) * rs  for a chunked view (rows come in
+// chunks of L, e.g. one chunk per source rank of an all-to-all buffer) and
+// i * rs  otherwise.
+struct View {
+  long long bs;    // batch stride
+  long long cs;    // chunk stride (chunked views)
+  int rs;          // row stride
+  int hs;          // head stride
+  int chunked;     // 0: row_off(i) = i * rs
+  FastDiv L;       // rows per chunk
+};
+
+__device__ __forceinline__ long long row_off(const View& v, int i) {
+  if (!v.chunked) return (long long)i * v.rs;
+  uint32_t c, r;
+  v.L.divmod(uint32_t(i), c, r);
+  return (long long)c * v.cs + (long long)r * v.rs;
+}
+
 struct AttnArgs {
+  View qv, kv, ov;  // Q, K and V (one view for both), O
   const __bf16* q;
   const __bf16* k;
   const __bf16* v;
@@ -149,9 +171,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   const int bh = work / a.m_tiles;
   const int h = bh % a.H;
   const int b = bh / a.H;
-  const size_t row_stride = size_t(a.H) * D;  // elements between consecutive sequence rows
-  const __bf16* kbase = a.k + (size_t(b) * a.Skv * a.H + h) * D;
-  const __bf16* vbase = a.v + (size_t(b) * a.Skv * a.H + h) * D;
+  const __bf16* kbase = a.k + b * a.kv.bs + h * a.kv.hs;
+  const __bf16* vbase = a.v + b * a.kv.bs + h * a.kv.hs;
   const uint8_t* mbase = a.mask ? a.mask + size_t(b) * a.Skv : nullptr;
 
   // ---- Q fragment (B operand of S^T = K Q^T): query row q_row, d = ks*16 + 8*hi .. +8
@@ -159,7 +180,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   bf16x8 qf[C::KS];
   {
     const bool ok = q_row < a.Sq;
-    const __bf16* qp = a.q + (size_t(b) * a.Sq + (ok ? q_row : 0)) * row_stride + size_t(h) * D;
+    const __bf16* qp = a.q + b * a.qv.bs + row_off(a.qv, ok ? q_row : 0) + h * a.qv.hs;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       bf16x8 t = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + 8 * hi);
@@ -178,8 +199,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // ---- HBM -> LDS fill.  Slot s of a tile (16 bytes) holds chunk
   // (s % CHUNKS) ^ swz(key) of row key = s / CHUNKS; instruction j of wave gw
   // fills slots [(gw*SPT + j)*64, +64), lane-ordered.
-  const uint32_t rs_bytes = uint32_t(row_stride) * 2u;
-  const uint32_t valid_end = uint32_t(a.Skv - 1) * rs_bytes + uint32_t(D) * 2u;
+  const uint32_t rs_bytes = uint32_t(a.kv.rs) * 2u;
   uint32_t goff[C::SPT];
 #pragma unroll
   for (int j = 0; j < C::SPT; ++j) {
@@ -189,11 +209,14 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     goff[j] = uint32_t(key) * rs_bytes + uint32_t(chunk) * 16u;
   }
   // dst: the destination tile array.
+  // The 64 rows of a tile are contiguous at stride rs (a chunked view has chunks
+  // of a multiple of 64 rows); rows past the last key are outside the range.
   auto fill = [&](const __bf16* base, int t, char* dst) {
-    const uint32_t off = uint32_t(t) * uint32_t(C::BN) * rs_bytes;
+    const int key0 = t * C::BN;
+    const int rows = min(C::BN, a.Skv - key0);
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(reinterpret_cast<const char*>(base)) + off, (short)0, int(valid_end - off),
-        0x00020000);
+        const_cast<__bf16*>(base + row_off(a.kv, key0)), (short)0,
+        int(uint32_t(rows - 1) * rs_bytes + uint32_t(D) * 2u), 0x00020000);
 #pragma unroll
     for (int j = 0; j < C::SPT; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -479,7 +502,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const float c0 = a0 * inv, c1 = a1 * inv;
     if (q_row < a.Sq) {
-      __bf16* op = a.o + (size_t(b) * a.Sq + q_row) * row_stride + size_t(h) * D;
+      __bf16* op = a.o + b * a.ov.bs + row_off(a.ov, q_row) + h * a.ov.hs;
       // Accumulator row r of block db is d = db*32 + 8*(r/4) + 4*hi + r%4.
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -552,7 +575,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   w[1] = (__bf16)(acc.y * inv);
   w[2] = (__bf16)(acc.z * inv);
   w[3] = (__bf16)(acc.w * inv);
-  *reinterpret_cast<bf16x4*>(a.o + (size_t(b) * a.Sq + q_row) * (size_t(a.H) * D) + size_t(h) * D + c4) = w;
+  *reinterpret_cast<bf16x4*>(a.o + b * a.ov.bs + row_off(a.ov, q_row) + h * a.ov.hs + c4) = w;
 }
 
 template <int D>
@@ -567,38 +590,49 @@ using namespace cpattn;
 
 namespace {
 
-// Validation, plan and launch shared by both entry points.
-int attn_run(const void* q, const void* k, const void* v, const uint8_t* key_mask, void* o, int64_t B,
-             int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale, int causal, void* ws, size_t ws_bytes,
-             cp_stream_t stream) {
-  if (!q || !k || !v || !o) return CP_ERR_NULL;
-  if (B < 1 || Sq < 1 || Skv < 1 || H < 1) return CP_ERR_SHAPE;
-  if (D != 64 && D != 128) return CP_ERR_HEAD_DIM;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return CP_ERR_SCALE;
-  if (causal != 0) return CP_ERR_UNSUPPORTED;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return CP_ERR_ALIGNMENT;
-  if (ws && !aligned16(ws)) return CP_ERR_ALIGNMENT;
-  // Per-dimension sizes and the work count are kept in int on the device.
-  constexpr int64_t kIntMax = 0x7fffffff;
-  if (B > kIntMax || Sq > kIntMax || Skv > kIntMax - 64 || H > kIntMax) return CP_ERR_SHAPE;
-  // K/V of one batch are addressed with 32-bit byte offsets.
-  if (Skv * H * D * 2 > kIntMax) return CP_ERR_SHAPE;
+View plain_view(int64_t S, int64_t H, int64_t D) {
+  View v;
+  v.bs = S * H * D;
+  v.cs = 0;
+  v.rs = int(H * D);
+  v.hs = int(D);
+  v.chunked = 0;
+  return v;
+}
+
+// Rows of S = W * L in W chunks of L rows: batch b, row i at
+// (i / L) * cs + b * bs + (i % L) * rs.  With one batch the chunks are
+// consecutive and the view is a plain strided one.
+View chunked_view(int64_t B, int64_t L, int64_t H, int64_t hs, int64_t rs) {
+  View v;
+  v.bs = L * rs;
+  v.cs = B * L * rs;
+  v.rs = int(rs);
+  v.hs = int(hs);
+  v.chunked = B > 1;
+  v.L = FastDiv(uint32_t(L));
+  (void)H;
+  return v;
+}
+
+// Split plan and launch.  Every argument has been validated; ext_* are the byte
+// extents of the operands, for the workspace overlap check.
+int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* v, const View& kv,
+                const uint8_t* key_mask, __bf16* o, const View& ov, int64_t B, int64_t Sq, int64_t Skv,
+                int64_t H, int64_t D, float scale, void* ws, size_t ws_bytes, size_t ext_q, size_t ext_kv,
+                size_t ext_o, cp_stream_t stream) {
   const int64_t bm = 32 * kGroupWaves;
   const int64_t m_tiles = (Sq + bm - 1) / bm;
-  int64_t bh, n_work, qe, ke;
-  if (!mul_capped(B, H, kIntMax, &bh) || !mul_capped(bh, m_tiles, kIntMax, &n_work)) return CP_ERR_SHAPE;
-  if (!mul_capped(B * Sq, H * D, int64_t(1) << 60, &qe) || !mul_capped(B * Skv, H * D, int64_t(1) << 60, &ke))
-    return CP_ERR_SHAPE;
-  const size_t qb = size_t(qe) * 2, kb = size_t(ke) * 2;
-  if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb)) return CP_ERR_ALIAS;
-  if (key_mask && overlaps(o, qb, key_mask, size_t(B * Skv))) return CP_ERR_ALIAS;
-
+  const int64_t n_work = B * H * m_tiles;
   AttnArgs args;
-  args.q = static_cast<const __bf16*>(q);
-  args.k = static_cast<const __bf16*>(k);
-  args.v = static_cast<const __bf16*>(v);
+  args.qv = qv;
+  args.kv = kv;
+  args.ov = ov;
+  args.q = q;
+  args.k = k;
+  args.v = v;
   args.mask = key_mask;
-  args.o = static_cast<__bf16*>(o);
+  args.o = o;
   args.B = int(B);
   args.Sq = int(Sq);
   args.Skv = int(Skv);
@@ -620,15 +654,17 @@ int attn_run(const void* q, const void* k, const void* v, const uint8_t* key_mas
     if (2 * n_work <= cus && nsplit >= 2) {
       const size_t need = size_t(n_work * nsplit) * size_t(bm) * size_t(D + 2) * sizeof(float);
       if (ws_bytes < need) return CP_ERR_WORKSPACE;
-      if (overlaps(ws, need, q, qb) || overlaps(ws, need, k, kb) || overlaps(ws, need, v, kb) ||
-          overlaps(ws, need, o, qb) || (key_mask && overlaps(ws, need, key_mask, size_t(B * Skv))))
+      if (overlaps(ws, need, q, ext_q) || overlaps(ws, need, k, ext_kv) || overlaps(ws, need, v, ext_kv) ||
+          overlaps(ws, need, o, ext_o) || (key_mask && overlaps(ws, need, key_mask, size_t(B * Skv))))
         return CP_ERR_ALIAS;
       args.nsplit = int(nsplit);
       args.ws = static_cast<float*>(ws);
     }
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const dim3 grid{unsigned(n_work * args.nsplit)}, block{unsigned(kThreads)}, cblock{256u}, cgrid{unsigned(n_work * (D / 8))};  // BM * D / 4 threads of 256 per block
+  // combine: BM * D / 4 threads of 256 per query block
+  const dim3 grid{unsigned(n_work * args.nsplit)}, block{unsigned(kThreads)}, cblock{256u},
+      cgrid{unsigned(n_work * (D / 8))};
   if (D == 128) {
     hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, block, 0, s, args);
     if (args.nsplit > 1) hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, cblock, 0, s, args);
@@ -637,6 +673,42 @@ int attn_run(const void* q, const void* k, const void* v, const uint8_t* key_mas
     if (args.nsplit > 1) hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, cblock, 0, s, args);
   }
   return hip_status(hipGetLastError());
+}
+
+// Checks shared by every attention entry point.
+int attn_check(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale, int causal) {
+  if (B < 1 || Sq < 1 || Skv < 1 || H < 1) return CP_ERR_SHAPE;
+  if (D != 64 && D != 128) return CP_ERR_HEAD_DIM;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return CP_ERR_SCALE;
+  if (causal != 0) return CP_ERR_UNSUPPORTED;
+  return CP_OK;
+}
+
+// Local-Q / global-KV attention on dense [B][S][H][D] operands.
+int attn_run(const void* q, const void* k, const void* v, const uint8_t* key_mask, void* o, int64_t B,
+             int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale, int causal, void* ws, size_t ws_bytes,
+             cp_stream_t stream) {
+  if (!q || !k || !v || !o) return CP_ERR_NULL;
+  if (const int st = attn_check(B, Sq, Skv, H, D, scale, causal)) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return CP_ERR_ALIGNMENT;
+  if (ws && !aligned16(ws)) return CP_ERR_ALIGNMENT;
+  // Per-dimension sizes and the work count are kept in int on the device.
+  constexpr int64_t kIntMax = 0x7fffffff;
+  if (B > kIntMax || Sq > kIntMax || Skv > kIntMax - 64 || H > kIntMax) return CP_ERR_SHAPE;
+  // Rows of a K/V tile are addressed with 32-bit byte offsets.
+  if (H * D * 2 * 64 > kIntMax) return CP_ERR_SHAPE;
+  const int64_t bm = 32 * kGroupWaves;
+  const int64_t m_tiles = (Sq + bm - 1) / bm;
+  int64_t bh, n_work, qe, ke;
+  if (!mul_capped(B, H, kIntMax, &bh) || !mul_capped(bh, m_tiles, kIntMax, &n_work)) return CP_ERR_SHAPE;
+  if (!mul_capped(B * Sq, H * D, int64_t(1) << 60, &qe) || !mul_capped(B * Skv, H * D, int64_t(1) << 60, &ke))
+    return CP_ERR_SHAPE;
+  const size_t qb = size_t(qe) * 2, kb = size_t(ke) * 2;
+  if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb)) return CP_ERR_ALIAS;
+  if (key_mask && overlaps(o, qb, key_mask, size_t(B * Skv))) return CP_ERR_ALIAS;
+  return attn_launch(static_cast<const __bf16*>(q), plain_view(Sq, H, D), static_cast<const __bf16*>(k),
+                     static_cast<const __bf16*>(v), plain_view(Skv, H, D), key_mask, static_cast<__bf16*>(o),
+                     plain_view(Sq, H, D), B, Sq, Skv, H, D, scale, ws, ws_bytes, qb, kb, qb, stream);
 }
 
 }  // namespace
@@ -653,6 +725,38 @@ extern "C" int cp_attn_localq_globalkv_ws(const void* q, const void* k, const vo
                                           int64_t Skv, int64_t H, int64_t D, float scale, int causal,
                                           void* workspace, size_t workspace_bytes, cp_stream_t stream) {
   return attn_run(q, k, v, key_mask, o, B, Sq, Skv, H, D, scale, causal, workspace, workspace_bytes, stream);
+}
+
+extern "C" int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, void* send, int64_t B,
+                                    int64_t S_local, int64_t H_local, int64_t D, int64_t W, float scale,
+                                    int causal, void* workspace, size_t workspace_bytes, cp_stream_t stream) {
+  if (!recv || !send) return CP_ERR_NULL;
+  if (W < 1) return CP_ERR_SHAPE;
+  constexpr int64_t kIntMax = 0x7fffffff;
+  if (S_local < 1 || S_local > kIntMax / W) return CP_ERR_SHAPE;
+  const int64_t S = W * S_local;
+  if (const int st = attn_check(B, S, S, H_local, D, scale, causal)) return st;
+  if (!aligned16(recv) || !aligned16(send)) return CP_ERR_ALIGNMENT;
+  if (workspace && !aligned16(workspace)) return CP_ERR_ALIGNMENT;
+  if (B > kIntMax || S > kIntMax - 64 || H_local > kIntMax) return CP_ERR_SHAPE;
+  if (H_local * 3 * D * 2 * 64 > kIntMax) return CP_ERR_SHAPE;
+  // With several batches the received rows of one batch come in W chunks of
+  // S_local rows; K/V tiles of 64 rows must not straddle two chunks.
+  if (B > 1 && S_local % 64 != 0) return CP_ERR_UNSUPPORTED;
+  const int64_t bm = 32 * kGroupWaves;
+  int64_t bh, n_work, re, se;
+  if (!mul_capped(B, H_local, kIntMax, &bh) || !mul_capped(bh, (S + bm - 1) / bm, kIntMax, &n_work))
+    return CP_ERR_SHAPE;
+  if (!mul_capped(B * S, H_local * 3 * D, int64_t(1) << 60, &re)) return CP_ERR_SHAPE;
+  se = re / 3;
+  const size_t rb = size_t(re) * 2, sb = size_t(se) * 2;
+  if (overlaps(send, sb, recv, rb)) return CP_ERR_ALIAS;
+  if (key_mask && overlaps(send, sb, key_mask, size_t(B * S))) return CP_ERR_ALIAS;
+  const View in = chunked_view(B, S_local, H_local, 3 * D, H_local * 3 * D);
+  const View out = chunked_view(B, S_local, H_local, D, H_local * D);
+  const __bf16* r = static_cast<const __bf16*>(recv);
+  return attn_launch(r, in, r + D, r + 2 * D, in, key_mask, static_cast<__bf16*>(send), out, B, S, S, H_local,
+                     D, scale, workspace, workspace_bytes, rb, rb, sb, stream);
 }
 
 extern "C" size_t cp_attn_workspace_bytes(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D) {

@@ -175,6 +175,49 @@ def cp_attn_localq_globalkv(q, k, v, key_mask=None, scale=None, out=None, causal
     return out
 
 
+def cp_attn_recv_to_send(recv, B: int, W: int, key_mask=None, scale=None, out=None, causal=False,
+                         stream=None, split=True, workspace=None) -> torch.Tensor:
+    """Ulysses attention straight from the received staging buffer into the send layout.
+
+    recv [W, B*S_l, H_l, 3D] bf16 -> send [W, B, S_l, H_l, D]: the attention of the
+    H_l heads over the whole sequence S = W*S_l, equal bit for bit to
+    unpack -> cp_attn_localq_globalkv -> cp_output_reverse(0).  key_mask: uint8/bool
+    [B, S] or None.  split / workspace as for cp_attn_localq_globalkv.
+    """
+    lib = _lib.load()
+    W_, rows, Hl, D3 = recv.shape
+    if W_ != W or rows % B or D3 % 3:
+        raise ValueError("recv shape does not match W / B")
+    if recv.dtype != torch.bfloat16:
+        raise TypeError("attention takes bfloat16")
+    Sl, D = rows // B, D3 // 3
+    S = W * Sl
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    mask_ptr = None
+    if key_mask is not None:
+        if key_mask.dtype not in (torch.uint8, torch.bool) or tuple(key_mask.shape) != (B, S):
+            raise ValueError("key_mask must be uint8/bool [B, W*S_l]")
+        mask_ptr = _dev(key_mask, "key_mask")
+    shape = (W, B, Sl, Hl, D)
+    if out is None:
+        out = torch.empty(shape, dtype=recv.dtype, device=recv.device)
+    if tuple(out.shape) != shape or out.dtype != recv.dtype:
+        raise ValueError(f"out must be {shape} {recv.dtype}")
+    ws_ptr, ws_bytes = None, 0
+    if split:
+        need = int(lib.cp_attn_workspace_bytes(B, S, S, Hl, D))
+        if workspace is None:
+            workspace = staging_buffer("attn_workspace", (max(need, 16),), torch.uint8, recv.device)
+        elif workspace.dtype != torch.uint8 or workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor")
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel()
+    _lib.check("cp_attn_recv_to_send", lib.cp_attn_recv_to_send(
+        _dev(recv, "recv"), mask_ptr, _dev(out, "send"), B, Sl, Hl, D, W, float(scale),
+        int(bool(causal)), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
 def cp_attn_workspace_bytes(B: int, Sq: int, Skv: int, H: int, D: int) -> int:
     """Workspace bytes cp_attn_localq_globalkv may use with split=True (upper bound, current device)."""
     return int(_lib.load().cp_attn_workspace_bytes(B, Sq, Skv, H, D))

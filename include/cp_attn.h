@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CP_ABI_VERSION 2
+#define CP_ABI_VERSION 3
 
 typedef struct ihipStream_t* cp_stream_t; /* == hipStream_t */
 
@@ -187,6 +187,37 @@ int cp_attn_localq_globalkv_ws(const void* q, const void* k, const void* v,
  * per compute unit).  0 for an unsupported D.  No GPU work, no allocation.
  */
 size_t cp_attn_workspace_bytes(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D);
+
+/*
+ * Ulysses attention fused with the steps on either side of it: the attention
+ * of this rank's H_local heads over the whole sequence S = W * S_local reads
+ * Q, K and V straight out of the received staging buffer (the unpack of
+ * cp_unpack_head_sharded becomes addressing, as the B == 1 "view, no copy"
+ * case of [sglang#33667]'s usp.py excerpt already is for the sequence axis),
+ * and writes O straight into the send layout of cp_output_reverse phase 0.
+ * The result equals
+ *
+ *   cp_unpack_head_sharded(recv) -> cp_attn_localq_globalkv(q, k, v) with
+ *   Sq = Skv = S, H = H_local -> cp_output_reverse(SEND)
+ *
+ * bit for bit, without the intermediate Q/K/V and O buffers.
+ *
+ *   recv      : [W][B*S_local][H_local][3*D] bf16 (q, k, v concatenated per head)
+ *   key_mask  : NULL, or [B][S] uint8 over the global key index r*S_local + s
+ *   send      : [W][B][S_local][H_local][D] bf16
+ *   workspace : as for cp_attn_localq_globalkv_ws (sized by
+ *               cp_attn_workspace_bytes(B, S, S, H_local, D)), or NULL
+ *
+ * Requires the attention's conditions (D in {64, 128}, scale, causal == 0),
+ * W >= 1, 16-byte aligned pointers, send disjoint from recv and key_mask, and
+ * S_local % 64 == 0 when B > 1 (CP_ERR_UNSUPPORTED otherwise: with several
+ * batches a batch's rows arrive in W chunks, and a 64-key tile must not span
+ * two of them).
+ */
+int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, void* send,
+                         int64_t B, int64_t S_local, int64_t H_local, int64_t D, int64_t W,
+                         float scale, int causal, void* workspace, size_t workspace_bytes,
+                         cp_stream_t stream);
 
 /*
  * Ulysses output exchange ([sglang#33667] names _usp_output_all_to_all in its

@@ -19,6 +19,12 @@ Two layouts, from [vllm-omni#7641] (commit message):
 
 The functions return every rank's result so that tests can check that the ranks'
 outputs, concatenated in global rank order, equal single-rank attention.
+
+A Ulysses rank's attention sits between its two exchanges ([sglang#33667],
+usp.py excerpt and implementation breakdown): it unpacks the received staging
+buffer into head-sharded Q/K/V, attends over the whole sequence for its H/W
+heads, and lays the output out for the reverse exchange.  ``ulysses_attention_send``
+is that composition, one step after the other.
 """
 
 from __future__ import annotations
@@ -83,3 +89,27 @@ def composed_2d(q_full, k_full, v_full, U, A, key_mask=None, scale=None):
         for u, g in enumerate(group):
             outputs[g] = res[u]
     return attn_inputs, outputs
+
+
+def ulysses_attention_send(recv, B, W, key_mask=None, scale=None):
+    """One Ulysses rank between its exchanges: received ``[W, B*S_l, H_l, 3D]`` ->
+    send layout ``[W, B, S_l, H_l, D]`` of the attention over all ``W*S_l`` rows
+    (unpack, then attention, then the send step of the output reverse)."""
+    q, k, v = _layout.unpack_head_sharded(recv, B, W)
+    o = _attn.attention(q, k, v, key_mask=key_mask, scale=scale)
+    return _layout.output_reverse_send(o, W)
+
+
+def ulysses_attention_all(q_full, k_full, v_full, W, key_mask=None, scale=None):
+    """Every rank of one Ulysses group: pack, exchange, ``ulysses_attention_send``,
+    exchange, merge.  Returns ``(recv, outputs)``: each rank's received staging
+    buffer and its final ``[B, S_l, H, D]`` output (its own rows, all heads)."""
+    B, S, H, D = q_full.shape
+    if S % W or H % W:
+        raise ValueError("S and H must divide by W")
+    Sl = S // W
+    shards = [tuple(t[:, r * Sl:(r + 1) * Sl] for t in (q_full, k_full, v_full)) for r in range(W)]
+    recv = _layout.exchange([_layout.pack_qkv_dst_major(*shards[r], W) for r in range(W)])
+    snd = [ulysses_attention_send(recv[j], B, W, key_mask, scale) for j in range(W)]
+    rcv = _layout.exchange(snd)
+    return recv, [_layout.output_reverse_merge(x) for x in rcv]

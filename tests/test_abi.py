@@ -97,6 +97,14 @@ def _attn_ws(**kw):
                                                   a["causal"], a["ws"], a["nbytes"], None)
 
 
+def _fused(**kw):
+    a = dict(r=A, m=None, s=A + BIG, B=1, Sl=128, Hl=2, D=128, W=2, scale=0.125, causal=0,
+             ws=None, nbytes=0)
+    a.update(kw)
+    return _lib.load().cp_attn_recv_to_send(a["r"], a["m"], a["s"], a["B"], a["Sl"], a["Hl"], a["D"],
+                                            a["W"], a["scale"], a["causal"], a["ws"], a["nbytes"], None)
+
+
 def _rev(**kw):
     a = dict(phase=0, s=A, d=A + BIG, B=1, Sl=4, Hl=2, D=128, W=2, dtype=BF16)
     a.update(kw)
@@ -180,6 +188,29 @@ def test_attention_rejects(kw, code):
 ])
 def test_attention_ws_rejects(kw, code):
     assert _attn_ws(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(r=None), _lib.CP_ERR_NULL),
+    (dict(s=None), _lib.CP_ERR_NULL),
+    (dict(W=0), _lib.CP_ERR_SHAPE),
+    (dict(Sl=0), _lib.CP_ERR_SHAPE),
+    (dict(B=0), _lib.CP_ERR_SHAPE),
+    (dict(D=96), _lib.CP_ERR_HEAD_DIM),
+    (dict(scale=0.0), _lib.CP_ERR_SCALE),
+    (dict(causal=1), _lib.CP_ERR_UNSUPPORTED),
+    (dict(r=A + 8), _lib.CP_ERR_ALIGNMENT),
+    (dict(ws=A + 5 * BIG + 8, nbytes=1 << 20), _lib.CP_ERR_ALIGNMENT),
+    (dict(s=A + 4096), _lib.CP_ERR_ALIAS),                      # send overlaps recv
+    (dict(m=A + BIG + 64), _lib.CP_ERR_ALIAS),                  # mask inside send
+    (dict(B=2, Sl=70), _lib.CP_ERR_UNSUPPORTED),                # chunks not a multiple of 64 rows
+    (dict(ws=A + 5 * BIG, nbytes=16, Sl=2048), _lib.CP_ERR_WORKSPACE),  # 2 heads x 32 blocks split
+    (dict(ws=A, nbytes=1 << 30, Sl=2048), _lib.CP_ERR_ALIAS),   # workspace overlaps recv
+    (dict(Sl=1 << 30, W=4), _lib.CP_ERR_SHAPE),
+])
+def test_recv_to_send_rejects(kw, code):
+    assert _fused(**kw) == code
 
 
 def test_workspace_bytes():

@@ -208,3 +208,72 @@ def test_split_kv_matches_oracle_and_unsplit(gu, B, H, Sq, Skv, D, masked):
         _assert_close(sel, ref, f"split sampled B{B} H{H} Sq{Sq} Skv{Skv}")
     # the two schedules sum the same terms in a different order
     assert np.abs(got - whole).max() <= 2e-2
+
+
+# ------------------------------------------- attention fused with unpack and send
+
+def _fused_ref_chain(cp, recv_d, B, W, md):
+    """The unfused GPU chain the fused entry point replaces."""
+    q, k, v = cp.cp_unpack_head_sharded(recv_d, B, W)
+    o = cp.cp_attn_localq_globalkv(q, k, v, md)
+    return cp.cp_output_reverse(0, o, W, B)
+
+
+@pytest.mark.parametrize("B,W,Sl,Hl,D,masked", [
+    (1, 2, 128, 2, 64, False),    # tiny-workload shape
+    (1, 3, 70, 2, 64, True),      # ragged: 210 rows, tiles and query blocks with tails
+    (1, 2, 33, 1, 128, False),    # fewer rows than one tile
+    (2, 2, 64, 3, 128, True),     # several batches: rows arrive in chunks of S_l
+    (2, 4, 128, 2, 128, False),
+    (3, 2, 192, 1, 64, True),
+])
+def test_recv_to_send_matches_oracle_and_unfused(gu, B, W, Sl, Hl, D, masked):
+    import context_attention_diffusion_amd as cp
+    from oracle import cp_share
+    seed = 7000 + B * 100 + W * 10 + Sl + D
+    recv = _rand_bits((W, B * Sl, Hl, 3 * D), seed)
+    S = W * Sl
+    mask = None
+    if masked:
+        mask = (np.random.default_rng(seed + 1).random((B, S)) > 0.3).astype(np.uint8)
+        mask[:, S - 1] = 1
+    rd = gu.to_dev(recv)
+    md = None if mask is None else torch.from_numpy(mask).to(gu.DEV)
+    print(f"[attn] recv_to_send B={B} W={W} Sl={Sl} Hl={Hl} D={D} masked={masked}", flush=True)
+    got = cp.cp_attn_recv_to_send(rd, B, W, md)
+    ref_gpu = _fused_ref_chain(cp, rd, B, W, md)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref_gpu), "fused result differs from unpack -> attention -> send"
+    ref = cp_share.ulysses_attention_send(bf16.bits_to_f64(recv), B, W, mask)
+    _assert_close(gu.to_f64(got), ref, f"recv_to_send B{B} W{W} Sl{Sl} Hl{Hl} D{D}")
+
+
+@pytest.mark.parametrize("name", ["image_cp4", "joint_cfg_cp4"])
+def test_recv_to_send_full_size_sampled(gu, name):
+    """Rank 0 of the workload's Ulysses group at full size: sampled rows against the
+    oracle, the whole output against the unfused chain."""
+    import context_attention_diffusion_amd as cp
+    from oracle import layout as OL
+    wl = workloads.WORKLOADS[name]
+    W, B, Sl, D = wl.W, wl.B, wl.S_local, wl.D
+    Hl = wl.H // W
+    full = workloads.global_qkv(wl)
+    shards = [tuple(np.ascontiguousarray(t[:, r * Sl:(r + 1) * Sl]) for t in full) for r in range(W)]
+    recv0 = OL.exchange([OL.pack_qkv_dst_major(*shards[r], W) for r in range(W)])[0]
+    mask = workloads.key_mask(wl)
+    rd = gu.to_dev(recv0)
+    md = None if mask is None else torch.from_numpy(mask).to(gu.DEV)
+    print(f"[attn] recv_to_send full {name}", flush=True)
+    got = cp.cp_attn_recv_to_send(rd, B, W, md)
+    ref_gpu = _fused_ref_chain(cp, rd, B, W, md)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref_gpu)
+    # rank 0 holds heads [0, Hl) of the sequence-concatenated global tensors
+    q, k, v = (bf16.bits_to_f64(np.ascontiguousarray(t[:, :, :Hl])) for t in full)
+    rng = np.random.default_rng(wl.seed + 5)
+    S = W * Sl
+    rows = [(int(rng.integers(B)), int(rng.integers(S)), int(rng.integers(Hl))) for _ in range(32)]
+    ref = OA.attention_rows(q, k, v, rows, mask, 1.0 / math.sqrt(D))
+    g = gu.to_f64(got)
+    sel = np.stack([g[i // Sl, b, i % Sl, h] for b, i, h in rows])
+    _assert_close(sel, ref, f"recv_to_send {name} sampled")

@@ -206,6 +206,27 @@ def test_2d_ranks_reassemble_full_attention(U, Ag, masked):
             np.testing.assert_array_equal(va, v[:, :, u * Hu:(u + 1) * Hu])
 
 
+@pytest.mark.parametrize("W", [2, 3])
+@pytest.mark.parametrize("masked", [False, True])
+def test_ulysses_attention_ranks_reassemble_full_attention(W, masked):
+    # Every rank attends its head slice over the whole sequence between the two
+    # exchanges; after the reverse exchange rank r holds rows r of full attention.
+    B, S, H, D = 2, 30, 6, 4
+    q, k, v = _rand((B, S, H, D), 44), _rand((B, S, H, D), 45), _rand((B, S, H, D), 46)
+    m = _mask(B, S, 47) if masked else None
+    recv, outs = cp_share.ulysses_attention_all(q, k, v, W, m)
+    np.testing.assert_allclose(np.concatenate(outs, axis=1), A.attention(q, k, v, m),
+                               rtol=1e-12, atol=1e-13)
+    # Rank j's send buffer, chunk r, is its heads' output for rows of rank r.
+    Sl, Hl = S // W, H // W
+    full = A.attention(q, k, v, m)
+    for j in range(W):
+        snd = cp_share.ulysses_attention_send(recv[j], B, W, m)
+        for r in range(W):
+            np.testing.assert_allclose(snd[r], full[:, r * Sl:(r + 1) * Sl, j * Hl:(j + 1) * Hl],
+                                       rtol=1e-12, atol=1e-13)
+
+
 def test_bf16_widening_is_exact():
     bits = np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0x4049, 0x7F80, 0x0001, 0x7F7F],
                     dtype=np.uint16)

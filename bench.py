@@ -23,6 +23,12 @@ rank's local Q shard against the resident global K/V (standing in for the K/V
 all-gather), and the output reverse runs on a resident head-sharded buffer of the
 Ulysses layout.
 
+For the workloads without an AllGather-KV stage the JSON also carries
+`ulysses_fused`: the Ulysses-only rank step (attention of the rank's H/W heads
+over the whole sequence, the same FLOPs) timed once with separate unpack and
+send steps and once with cp_attn_recv_to_send, which reads Q/K/V from the
+received buffer and writes the send layout directly.
+
 Prints one JSON line.  `value` is attention TFLOP/s over the whole step
 (algorithmic attention FLOPs / step time), with the step captured once into a
 HIP graph and replayed (`--eager` launches it op by op).  Per-kernel durations
@@ -374,6 +380,61 @@ def kernel_bursts(path, only=None, burst=20):
     return res
 
 
+def ulysses_chain(path, burst=10):
+    """Ulysses-only rank step (no AllGather-KV), unfused and fused, on the step's buffers.
+
+    unfused: pack -> exchange -> unpack -> attention of the rank's H/W heads over the
+             whole sequence -> send layout -> exchange -> merge
+    fused:   pack -> exchange -> cp_attn_recv_to_send -> exchange -> merge
+    Both attentions do the same FLOPs as the workload's local-Q/global-KV share.
+    Returns step and attention durations (us, graph-replayed bursts) and whether the
+    two chains' send buffers are bit-identical."""
+    import torch
+    cp, wl = path.cp, path.wl
+    W, B = wl.W, wl.B
+    o_u = torch.empty_like(path.q_hs)
+    snd_u = torch.empty_like(path.snd)
+    snd_f = torch.empty_like(path.snd)
+
+    def attn_unfused():
+        cp.cp_attn_localq_globalkv(path.q_hs, path.k_hs, path.v_hs, path.mask, scale=path.scale, out=o_u)
+
+    def send_unfused():
+        if B == 1:
+            return o_u.view(snd_u.shape)
+        return cp.cp_output_reverse(0, o_u, W, B, out=snd_u)
+
+    def attn_fused():
+        cp.cp_attn_recv_to_send(path.recv, B, W, path.mask, scale=path.scale, out=snd_f)
+
+    def step_unfused():
+        path.pack()
+        path.exchange_in()
+        path.unpack()
+        attn_unfused()
+        path.exchange_out(send_unfused())
+        path.merge()
+
+    def step_fused():
+        path.pack()
+        path.exchange_in()
+        attn_fused()
+        path.exchange_out(snd_f)
+        path.merge()
+
+    step_unfused()
+    step_fused()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(send_unfused(), snd_f))
+    res = {"unfused_step_us": time_burst(step_unfused, burst) * 1e3,
+           "fused_step_us": time_burst(step_fused, burst) * 1e3,
+           "unfused_attn_us": time_burst(attn_unfused, burst) * 1e3,
+           "fused_attn_us": time_burst(attn_fused, burst) * 1e3,
+           "fused_send_equals_unfused": same}
+    res["step_speedup"] = res["unfused_step_us"] / res["fused_step_us"]
+    return res
+
+
 ATTN_SRC = os.path.join(ROOT, "context_attention_diffusion_amd", "csrc", "cp_attention.hip")
 CALIB_BYTES = 256 << 20
 
@@ -536,6 +597,13 @@ def main():
                               "pack_frac_hbm_peak": pc / PEAK_HBM_GBPS,
                               "unpack_frac_hbm_peak": uc / PEAK_HBM_GBPS,
                               "note": "rotating buffer sets, over 600 MB of reads per pass (misses the 256 MB MALL)"}
+    if args.only is None and not path.two_d:
+        u = ulysses_chain(path)
+        u["fused_attn_TFLOPs"] = flops / (u["fused_attn_us"] * 1e-6) / 1e12
+        u["fused_step_TFLOPs"] = flops / (u["fused_step_us"] * 1e-6) / 1e12
+        u["note"] = ("Ulysses-only rank step: attention of H/W heads over all W*S_l rows, "
+                     "same FLOPs as the local-Q/global-KV share")
+        out["ulysses_fused"] = u
     if args.only is None:
         out["parity"] = parity_sample(path, wl)
         if not args.no_cpu_baseline:

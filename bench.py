@@ -23,6 +23,9 @@ rank's local Q shard against the resident global K/V (standing in for the K/V
 all-gather), and the output reverse runs on a resident head-sharded buffer of the
 Ulysses layout.
 
+`chunked_kv` times the same share with its K/V arriving in W chunks
+(cp_attn_partial per chunk, then cp_attn_merge).
+
 For the workloads without an AllGather-KV stage the JSON also carries
 `ulysses_fused`: the Ulysses-only rank step (attention of the rank's H/W heads
 over the whole sequence, the same FLOPs) timed once with separate unpack and
@@ -435,6 +438,42 @@ def ulysses_chain(path, burst=10):
     return res
 
 
+def chunked_kv(path, burst=10):
+    """The local-Q/global-KV share with K/V arriving in W chunks (one per AllGather
+    rank): W cp_attn_partial calls and one cp_attn_merge, against the dense call."""
+    import torch
+    cp, wl = path.cp, path.wl
+    W, Sl = wl.W, wl.S_local
+    q, k, v = path.attn_q, path.attn_k, path.attn_v
+    B, Sq, H, D = q.shape
+    ks = [k[:, r * Sl:(r + 1) * Sl].contiguous() for r in range(W)]
+    vs = [v[:, r * Sl:(r + 1) * Sl].contiguous() for r in range(W)]
+    ms = [None if path.mask is None else path.mask[:, r * Sl:(r + 1) * Sl].contiguous() for r in range(W)]
+    o_parts = torch.empty((W, B, Sq, H, D), dtype=torch.float32, device=q.device)
+    lses = torch.empty((W, B, H, Sq), dtype=torch.float32, device=q.device)
+    out = torch.empty_like(q)
+
+    def partials():
+        for r in range(W):
+            cp.cp_attn_partial(q, ks[r], vs[r], ms[r], scale=path.scale, out=o_parts[r], lse=lses[r])
+
+    def merge():
+        cp.cp_attn_merge(o_parts, lses, out=out)
+
+    partials()
+    merge()
+    torch.cuda.synchronize()
+    dense = path.o_attn
+    path.attn()
+    torch.cuda.synchronize()
+    res = {"chunks": W, "partials_us": time_burst(partials, burst) * 1e3,
+           "merge_us": time_burst(merge, burst) * 1e3,
+           "merge_bytes": int(o_parts.numel() * 4 + lses.numel() * 4 + out.numel() * 2),
+           "max_abs_diff_vs_dense": float((out.float() - dense.float()).abs().max())}
+    res["merge_GBps"] = res["merge_bytes"] / (res["merge_us"] * 1e-6) / 1e9
+    return res
+
+
 ATTN_SRC = os.path.join(ROOT, "context_attention_diffusion_amd", "csrc", "cp_attention.hip")
 CALIB_BYTES = 256 << 20
 
@@ -604,6 +643,12 @@ def main():
         u["note"] = ("Ulysses-only rank step: attention of H/W heads over all W*S_l rows, "
                      "same FLOPs as the local-Q/global-KV share")
         out["ulysses_fused"] = u
+        c = chunked_kv(path)
+        c["total_us"] = c["partials_us"] + c["merge_us"]
+        c["dense_us"] = kern["attn"]["us"] if "attn" in kern else None
+        c["note"] = ("local-Q/global-KV share with K/V in W chunks: W partial attentions "
+                     "(fp32 O + lse) and one merge, against the dense call")
+        out["chunked_kv"] = c
     if args.only is None:
         out["parity"] = parity_sample(path, wl)
         if not args.no_cpu_baseline:

@@ -138,6 +138,10 @@ struct AttnArgs {
   int n_iter_blk;      // iterations per query block: ceil(ceil(Skv / BN) / 2)
   float* ws;           // partial states, slot = query block * nsplit + part:
                        // O [n_work * nsplit][BM][D] fp32, then (m, l) [n_work * nsplit][BM][2]
+  // Partial-attention output (instead of o): normalised O [B][Sq][H][D] fp32 and
+  // lse = ln(sum of exp(scale q.k) over the valid keys) [B][H][Sq] fp32.
+  float* o_part;
+  float* lse;
 };
 
 // The body is a device function behind a thin kernel: the LDS address-space
@@ -501,6 +505,27 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     }
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const float c0 = a0 * inv, c1 = a1 * inv;
+    if (a.o_part != nullptr) {
+      if (q_row < a.Sq) {
+        float* pp = a.o_part + ((size_t(b) * a.Sq + q_row) * a.H + h) * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float4 w;
+            w.x = acc_o[db][4 * g + 0] * c0 + comb[slot(db * 16 + 4 * g + 0)] * c1;
+            w.y = acc_o[db][4 * g + 1] * c0 + comb[slot(db * 16 + 4 * g + 1)] * c1;
+            w.z = acc_o[db][4 * g + 2] * c0 + comb[slot(db * 16 + 4 * g + 2)] * c1;
+            w.w = acc_o[db][4 * g + 3] * c0 + comb[slot(db * 16 + 4 * g + 3)] * c1;
+            *reinterpret_cast<float4*>(pp + db * 32 + 8 * g + 4 * hi) = w;
+          }
+        // sum_j e^{z_j} = 2^mm * l_tot, with mm and l_tot in the kernel's log2 units
+        if (hi == 0)
+          a.lse[(size_t(b) * a.H + h) * a.Sq + q_row] =
+              l_tot > 0.f ? (mm + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+      }
+      return;
+    }
     if (q_row < a.Sq) {
       __bf16* op = a.o + b * a.ov.bs + row_off(a.ov, q_row) + h * a.ov.hs;
       // Accumulator row r of block db is d = db*32 + 8*(r/4) + 4*hi + r%4.
@@ -578,6 +603,54 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   *reinterpret_cast<bf16x4*>(a.o + b * a.ov.bs + row_off(a.ov, q_row) + h * a.ov.hs + c4) = w;
 }
 
+// Merge of N partial attentions of the same queries over disjoint key sets:
+// O = sum_k e^{lse_k - L} O_k with L = ln sum_k e^{lse_k}; rows with no valid key
+// in any part (every lse_k = -inf) get zeros.  One thread per four columns.
+struct MergeArgs {
+  const float* o_parts;  // [N][B][Sq][H][D]
+  const float* lses;     // [N][B][H][Sq]
+  __bf16* o;             // [B][Sq][H][D]
+  int N, B, Sq, H, D;
+  long long rows;        // B * Sq * H
+};
+
+__global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
+  const int tpr = a.D / 4;
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long r = t / tpr;
+  if (r >= a.rows) return;
+  const int c4 = int(t % tpr) * 4;
+  const int h = int(r % a.H);
+  const long long bi = r / a.H;
+  const int i = int(bi % a.Sq), b = int(bi / a.Sq);
+  const long long lse_stride = (long long)a.B * a.H * a.Sq;
+  const long long lse0 = ((long long)b * a.H + h) * a.Sq + i;
+  const long long o_stride = a.rows * a.D;
+  float M = -INFINITY;
+  for (int k = 0; k < a.N; ++k) M = fmaxf(M, a.lses[k * lse_stride + lse0]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.f;
+  if (M != -INFINITY) {
+    for (int k = 0; k < a.N; ++k) {
+      const float lk = a.lses[k * lse_stride + lse0];
+      const float f = lk == -INFINITY ? 0.f : expf(lk - M);
+      const float4 x = *reinterpret_cast<const float4*>(a.o_parts + k * o_stride + r * a.D + c4);
+      L += f;
+      acc.x += f * x.x;
+      acc.y += f * x.y;
+      acc.z += f * x.z;
+      acc.w += f * x.w;
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  bf16x4 w;
+  w[0] = (__bf16)(acc.x * inv);
+  w[1] = (__bf16)(acc.y * inv);
+  w[2] = (__bf16)(acc.z * inv);
+  w[3] = (__bf16)(acc.w * inv);
+  *reinterpret_cast<bf16x4*>(a.o + r * a.D + c4) = w;
+}
+
 template <int D>
 __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(AttnArgs a) {
   attn_fwd_body<D>(a);
@@ -620,7 +693,7 @@ View chunked_view(int64_t B, int64_t L, int64_t H, int64_t hs, int64_t rs) {
 int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* v, const View& kv,
                 const uint8_t* key_mask, __bf16* o, const View& ov, int64_t B, int64_t Sq, int64_t Skv,
                 int64_t H, int64_t D, float scale, void* ws, size_t ws_bytes, size_t ext_q, size_t ext_kv,
-                size_t ext_o, cp_stream_t stream) {
+                size_t ext_o, cp_stream_t stream, float* o_part = nullptr, float* lse = nullptr) {
   const int64_t bm = 32 * kGroupWaves;
   const int64_t m_tiles = (Sq + bm - 1) / bm;
   const int64_t n_work = B * H * m_tiles;
@@ -644,6 +717,8 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
   args.n_iter_blk = int((n_tiles + 1) / 2);
   args.nsplit = 1;
   args.ws = nullptr;
+  args.o_part = o_part;
+  args.lse = lse;
   // Split the key range of every query block into nsplit parts when the query
   // blocks alone would occupy at most half of the compute units; each part
   // keeps at least kMinSplitIters iterations.
@@ -757,6 +832,67 @@ extern "C" int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, v
   const __bf16* r = static_cast<const __bf16*>(recv);
   return attn_launch(r, in, r + D, r + 2 * D, in, key_mask, static_cast<__bf16*>(send), out, B, S, S, H_local,
                      D, scale, workspace, workspace_bytes, rb, rb, sb, stream);
+}
+
+extern "C" int cp_attn_partial(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                               void* o_part, void* lse, int64_t B, int64_t Sq, int64_t Skv, int64_t H,
+                               int64_t D, float scale, int causal, cp_stream_t stream) {
+  if (!q || !k || !v || !o_part || !lse) return CP_ERR_NULL;
+  if (const int st = attn_check(B, Sq, Skv, H, D, scale, causal)) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part)) return CP_ERR_ALIGNMENT;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return CP_ERR_ALIGNMENT;
+  constexpr int64_t kIntMax = 0x7fffffff;
+  if (B > kIntMax || Sq > kIntMax || Skv > kIntMax - 64 || H > kIntMax) return CP_ERR_SHAPE;
+  if (H * D * 2 * 64 > kIntMax) return CP_ERR_SHAPE;
+  const int64_t bm = 32 * kGroupWaves;
+  int64_t bh, n_work, qe, ke;
+  if (!mul_capped(B, H, kIntMax, &bh) || !mul_capped(bh, (Sq + bm - 1) / bm, kIntMax, &n_work))
+    return CP_ERR_SHAPE;
+  if (!mul_capped(B * Sq, H * D, int64_t(1) << 59, &qe) || !mul_capped(B * Skv, H * D, int64_t(1) << 60, &ke))
+    return CP_ERR_SHAPE;
+  const size_t qb = size_t(qe) * 2, kb = size_t(ke) * 2, pb = size_t(qe) * 4, lb = size_t(B * H * Sq) * 4;
+  const size_t mb = key_mask ? size_t(B * Skv) : 0;
+  for (const auto& out : {std::make_pair(static_cast<const void*>(o_part), pb),
+                          std::make_pair(static_cast<const void*>(lse), lb)}) {
+    if (overlaps(out.first, out.second, q, qb) || overlaps(out.first, out.second, k, kb) ||
+        overlaps(out.first, out.second, v, kb) || (key_mask && overlaps(out.first, out.second, key_mask, mb)))
+      return CP_ERR_ALIAS;
+  }
+  if (overlaps(o_part, pb, lse, lb)) return CP_ERR_ALIAS;
+  return attn_launch(static_cast<const __bf16*>(q), plain_view(Sq, H, D), static_cast<const __bf16*>(k),
+                     static_cast<const __bf16*>(v), plain_view(Skv, H, D), key_mask, nullptr,
+                     plain_view(Sq, H, D), B, Sq, Skv, H, D, scale, nullptr, 0, qb, kb, pb, stream,
+                     static_cast<float*>(o_part), static_cast<float*>(lse));
+}
+
+extern "C" int cp_attn_merge(const void* o_parts, const void* lses, int64_t N, void* o, int64_t B, int64_t Sq,
+                             int64_t H, int64_t D, cp_stream_t stream) {
+  if (!o_parts || !lses || !o) return CP_ERR_NULL;
+  if (N < 1 || B < 1 || Sq < 1 || H < 1) return CP_ERR_SHAPE;
+  if (D != 64 && D != 128) return CP_ERR_HEAD_DIM;
+  if (!aligned16(o_parts) || !aligned16(o)) return CP_ERR_ALIGNMENT;
+  if ((reinterpret_cast<uintptr_t>(lses) & 3u) != 0) return CP_ERR_ALIGNMENT;
+  constexpr int64_t kIntMax = 0x7fffffff;
+  int64_t rows, total;
+  if (N > kIntMax || B > kIntMax || Sq > kIntMax || H > kIntMax) return CP_ERR_SHAPE;
+  if (!mul_capped(B * Sq, H, int64_t(1) << 40, &rows) || !mul_capped(rows, N * D, int64_t(1) << 58, &total))
+    return CP_ERR_SHAPE;
+  const size_t ob = size_t(rows * D) * 2, pb = size_t(total) * 4, lb = size_t(rows * N) * 4;
+  if (overlaps(o, ob, o_parts, pb) || overlaps(o, ob, lses, lb)) return CP_ERR_ALIAS;
+  MergeArgs m;
+  m.o_parts = static_cast<const float*>(o_parts);
+  m.lses = static_cast<const float*>(lses);
+  m.o = static_cast<__bf16*>(o);
+  m.N = int(N);
+  m.B = int(B);
+  m.Sq = int(Sq);
+  m.H = int(H);
+  m.D = int(D);
+  m.rows = rows;
+  const int64_t threads = rows * (D / 4);
+  const dim3 grid{unsigned((threads + 255) / 256)}, block{256u};
+  hipLaunchKernelGGL(attn_merge_kernel, grid, block, 0, reinterpret_cast<hipStream_t>(stream), m);
+  return hip_status(hipGetLastError());
 }
 
 extern "C" size_t cp_attn_workspace_bytes(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D) {

@@ -175,6 +175,54 @@ def cp_attn_localq_globalkv(q, k, v, key_mask=None, scale=None, out=None, causal
     return out
 
 
+def cp_attn_partial(q, k, v, key_mask=None, scale=None, out=None, lse=None, causal=False,
+                    stream=None):
+    """Attention over one K/V chunk: (o_part fp32 [B,Sq,H,D], lse fp32 [B,H,Sq], natural log).
+
+    Merge the partial results of disjoint key chunks with cp_attn_merge."""
+    lib = _lib.load()
+    B, Sq, H, D = q.shape
+    Skv = k.shape[1]
+    if k.shape != (B, Skv, H, D) or v.shape != k.shape:
+        raise ValueError("k, v must be [B, Skv, H, D] matching q")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("attention takes bfloat16 q, k, v")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    mask_ptr = None
+    if key_mask is not None:
+        if key_mask.dtype not in (torch.uint8, torch.bool) or tuple(key_mask.shape) != (B, Skv):
+            raise ValueError("key_mask must be uint8/bool [B, Skv]")
+        mask_ptr = _dev(key_mask, "key_mask")
+    if out is None:
+        out = torch.empty((B, Sq, H, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (B, Sq, H, D) or out.dtype != torch.float32:
+        raise ValueError("out must be float32 [B, Sq, H, D]")
+    if tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, Sq]")
+    _lib.check("cp_attn_partial", lib.cp_attn_partial(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), mask_ptr, _dev(out, "o_part"), _dev(lse, "lse"),
+        B, Sq, Skv, H, D, float(scale), int(bool(causal)), _stream(stream)))
+    return out, lse
+
+
+def cp_attn_merge(o_parts, lses, out=None, stream=None) -> torch.Tensor:
+    """Merge partial results: o_parts fp32 [N,B,Sq,H,D], lses fp32 [N,B,H,Sq] -> bf16 [B,Sq,H,D]."""
+    lib = _lib.load()
+    N, B, Sq, H, D = o_parts.shape
+    if o_parts.dtype != torch.float32 or lses.dtype != torch.float32 or tuple(lses.shape) != (N, B, H, Sq):
+        raise ValueError("o_parts must be float32 [N,B,Sq,H,D] and lses float32 [N,B,H,Sq]")
+    if out is None:
+        out = torch.empty((B, Sq, H, D), dtype=torch.bfloat16, device=o_parts.device)
+    if tuple(out.shape) != (B, Sq, H, D) or out.dtype != torch.bfloat16:
+        raise ValueError("out must be bfloat16 [B, Sq, H, D]")
+    _lib.check("cp_attn_merge", lib.cp_attn_merge(
+        _dev(o_parts, "o_parts"), _dev(lses, "lses"), N, _dev(out, "o"), B, Sq, H, D, _stream(stream)))
+    return out
+
+
 def cp_attn_recv_to_send(recv, B: int, W: int, key_mask=None, scale=None, out=None, causal=False,
                          stream=None, split=True, workspace=None) -> torch.Tensor:
     """Ulysses attention straight from the received staging buffer into the send layout.

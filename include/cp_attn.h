@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CP_ABI_VERSION 3
+#define CP_ABI_VERSION 4
 
 typedef struct ihipStream_t* cp_stream_t; /* == hipStream_t */
 
@@ -187,6 +187,45 @@ int cp_attn_localq_globalkv_ws(const void* q, const void* k, const void* v,
  * per compute unit).  0 for an unsupported D.  No GPU work, no allocation.
  */
 size_t cp_attn_workspace_bytes(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D);
+
+/*
+ * Attention over keys that arrive in chunks: a forward pass over one K/V chunk
+ * that also returns the log-sum-exp, and a merge of such partial results (the
+ * forward / merge split of [chitu-fastcp] FAQ and section 5; the
+ * [vllm-omni#7641] "Recommended follow-up" note on attending to gathered K/V
+ * as it arrives).  With z_ij = scale * q_i . k_j over the chunk's valid keys:
+ *
+ *   lse[b][h][i]     = ln sum_j exp(z_ij)           (-inf if the chunk has no valid key)
+ *   o_part[b][i][h]  = sum_j exp(z_ij - lse) v_j     (zeros if no valid key)
+ *
+ *   q            : [B][Sq][H][D] bf16;  k, v : [B][Skv][H][D] bf16 (this chunk)
+ *   key_mask     : NULL or [B][Skv] uint8 for this chunk, nonzero = attend
+ *   o_part       : [B][Sq][H][D] fp32, 16-byte aligned
+ *   lse          : [B][H][Sq] fp32, 4-byte aligned
+ *
+ * Same arithmetic and conditions as cp_attn_localq_globalkv (bf16
+ * probabilities, fp32 accumulation); o_part and lse must not overlap each
+ * other or any input.
+ */
+int cp_attn_partial(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                    void* o_part, void* lse, int64_t B, int64_t Sq, int64_t Skv, int64_t H,
+                    int64_t D, float scale, int causal, cp_stream_t stream);
+
+/*
+ * Merge of N partial results of the same queries over disjoint key sets:
+ *
+ *   L = ln sum_k exp(lse_k),   o = sum_k exp(lse_k - L) o_part_k   (bf16, RNE)
+ *
+ * Rows whose lse is -inf in every part (no valid key anywhere) get zeros.
+ *
+ *   o_parts : [N][B][Sq][H][D] fp32, 16-byte aligned
+ *   lses    : [N][B][H][Sq] fp32, 4-byte aligned
+ *   o       : [B][Sq][H][D] bf16, 16-byte aligned, disjoint from both inputs
+ *
+ * Requires N, B, Sq, H >= 1 and D in {64, 128}.
+ */
+int cp_attn_merge(const void* o_parts, const void* lses, int64_t N, void* o,
+                  int64_t B, int64_t Sq, int64_t H, int64_t D, cp_stream_t stream);
 
 /*
  * Ulysses attention fused with the steps on either side of it: the attention

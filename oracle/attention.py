@@ -118,3 +118,67 @@ def attention_loops(q, k, v, key_mask=None, scale=None):
                         num += wj * float(v[b, j, h, d])
                     out[b, i, h, d] = num / den
     return out
+
+
+# ------------------------------------------------ attention over key chunks, merged
+#
+# Attention over keys that arrive in chunks ([chitu-fastcp] FAQ and section 5: a
+# forward over each K/V chunk that also returns the log-sum-exp, then a merge;
+# [vllm-omni#7641]'s follow-up note on overlapping the K/V gather the same way):
+#
+#   lse_i  = ln sum_{j in V_b} exp(z_ij)                (-inf when V_b is empty)
+#   o_i    = sum_{j in V_b} exp(z_ij - lse_i) v_j        (zeros when V_b is empty)
+#
+# and for parts k = 1..N over disjoint key sets, with L_i = ln sum_k exp(lse_k,i):
+#
+#   o_i    = sum_k exp(lse_k,i - L_i) o_k,i              (zeros when every lse_k,i = -inf)
+#
+# which equals attention over the union of the keys.
+
+
+def attention_partial(q, k, v, key_mask=None, scale=None, chunk=256):
+    """Normalised output ``[B, Sq, H, D]`` and ``lse`` ``[B, H, Sq]`` (natural log) over these keys."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    _check(q, k, v, key_mask)
+    B, Sq, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = np.zeros((B, Sq, H, D), dtype=np.float64)
+    lse = np.full((B, H, Sq), -np.inf, dtype=np.float64)
+    for b in range(B):
+        valid = np.ones(k.shape[1], dtype=bool) if key_mask is None else (key_mask[b] != 0)
+        if not valid.any():
+            continue
+        for h in range(H):
+            kb = k[b][valid, h, :]
+            vb = v[b][valid, h, :]
+            for i0 in range(0, Sq, chunk):
+                z = scale * (q[b, i0:i0 + chunk, h, :] @ kb.T)
+                m = z.max(axis=1, keepdims=True)
+                e = np.exp(z - m)
+                s = e.sum(axis=1, keepdims=True)
+                out[b, i0:i0 + chunk, h, :] = (e @ vb) / s
+                lse[b, h, i0:i0 + chunk] = (m + np.log(s))[:, 0]
+    return out, lse
+
+
+def merge_partials(o_parts, lses):
+    """``o_parts`` ``[N, B, Sq, H, D]`` and ``lses`` ``[N, B, H, Sq]`` -> merged ``[B, Sq, H, D]``."""
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    N, B, Sq, H, D = o_parts.shape
+    if lses.shape != (N, B, H, Sq):
+        raise ValueError("lses must be [N, B, H, Sq]")
+    out = np.zeros((B, Sq, H, D), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for i in range(Sq):
+                lk = lses[:, b, h, i]
+                if np.all(lk == -np.inf):
+                    continue
+                m = lk.max()
+                w = np.exp(lk - m)
+                out[b, i, h, :] = (w[:, None] * o_parts[:, b, i, h, :]).sum(axis=0) / w.sum()
+    return out

@@ -105,6 +105,20 @@ def _fused(**kw):
                                             a["W"], a["scale"], a["causal"], a["ws"], a["nbytes"], None)
 
 
+def _partial(**kw):
+    a = dict(q=A, k=A + BIG, v=A + 2 * BIG, m=None, o=A + 3 * BIG, lse=A + 4 * BIG, B=1, Sq=8, Skv=16,
+             H=2, D=128, scale=0.125, causal=0)
+    a.update(kw)
+    return _lib.load().cp_attn_partial(a["q"], a["k"], a["v"], a["m"], a["o"], a["lse"], a["B"], a["Sq"],
+                                       a["Skv"], a["H"], a["D"], a["scale"], a["causal"], None)
+
+
+def _merge(**kw):
+    a = dict(p=A, l=A + BIG, N=2, o=A + 2 * BIG, B=1, Sq=8, H=2, D=128)
+    a.update(kw)
+    return _lib.load().cp_attn_merge(a["p"], a["l"], a["N"], a["o"], a["B"], a["Sq"], a["H"], a["D"], None)
+
+
 def _rev(**kw):
     a = dict(phase=0, s=A, d=A + BIG, B=1, Sl=4, Hl=2, D=128, W=2, dtype=BF16)
     a.update(kw)
@@ -211,6 +225,41 @@ def test_attention_ws_rejects(kw, code):
 ])
 def test_recv_to_send_rejects(kw, code):
     assert _fused(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=None), _lib.CP_ERR_NULL),
+    (dict(lse=None), _lib.CP_ERR_NULL),
+    (dict(Skv=0), _lib.CP_ERR_SHAPE),
+    (dict(D=96), _lib.CP_ERR_HEAD_DIM),
+    (dict(scale=-1.0), _lib.CP_ERR_SCALE),
+    (dict(causal=1), _lib.CP_ERR_UNSUPPORTED),
+    (dict(o=A + 3 * BIG + 8), _lib.CP_ERR_ALIGNMENT),
+    (dict(lse=A + 4 * BIG + 2), _lib.CP_ERR_ALIGNMENT),
+    (dict(o=A + 16), _lib.CP_ERR_ALIAS),              # o_part overlaps q
+    (dict(lse=A + BIG + 64), _lib.CP_ERR_ALIAS),      # lse inside k
+    (dict(lse=A + 3 * BIG + 64), _lib.CP_ERR_ALIAS),  # lse inside o_part
+    (dict(m=A + 4 * BIG + 4), _lib.CP_ERR_ALIAS),     # mask inside lse
+])
+def test_partial_rejects(kw, code):
+    assert _partial(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(p=None), _lib.CP_ERR_NULL),
+    (dict(o=None), _lib.CP_ERR_NULL),
+    (dict(N=0), _lib.CP_ERR_SHAPE),
+    (dict(Sq=0), _lib.CP_ERR_SHAPE),
+    (dict(D=32), _lib.CP_ERR_HEAD_DIM),
+    (dict(p=A + 4), _lib.CP_ERR_ALIGNMENT),
+    (dict(l=A + BIG + 1), _lib.CP_ERR_ALIGNMENT),
+    (dict(o=A + 64), _lib.CP_ERR_ALIAS),              # o inside o_parts
+    (dict(o=A + BIG), _lib.CP_ERR_ALIAS),             # o over lses
+])
+def test_merge_rejects(kw, code):
+    assert _merge(**kw) == code
 
 
 def test_workspace_bytes():

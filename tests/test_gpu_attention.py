@@ -277,3 +277,83 @@ def test_recv_to_send_full_size_sampled(gu, name):
     g = gu.to_f64(got)
     sel = np.stack([g[i // Sl, b, i % Sl, h] for b, i, h in rows])
     _assert_close(sel, ref, f"recv_to_send {name} sampled")
+
+
+# ------------------------------------------ attention over K/V chunks, then merge
+
+# The row sum adds bf16-rounded probabilities (each within 2^-9 relative of the
+# exact value), so ln(sum) is within about 2^-9 of the exact log-sum-exp; the
+# bound below allows twice that plus fp32 rounding.
+LSE_ERR = 5e-3
+
+
+def _partials(cp, qd, k, v, mask, edges):
+    outs, lses = [], []
+    for a, b in zip(edges[:-1], edges[1:]):
+        kd = torch.from_numpy(np.ascontiguousarray(k[:, a:b]).view(np.int16)).view(torch.bfloat16).to(qd.device)
+        vd = torch.from_numpy(np.ascontiguousarray(v[:, a:b]).view(np.int16)).view(torch.bfloat16).to(qd.device)
+        md = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask[:, a:b])).to(qd.device)
+        o, l = cp.cp_attn_partial(qd, kd, vd, md)
+        outs.append(o)
+        lses.append(l)
+    return torch.stack(outs), torch.stack(lses)
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,D,cuts,masked", [
+    (1, 2, 130, 1133, 128, (100, 433), False),
+    (2, 3, 70, 300, 64, (64,), True),
+    (1, 1, 5, 200, 128, (1, 2, 150), True),
+    (2, 2, 257, 700, 128, (350,), False),
+])
+def test_partial_and_merge_match_oracle(gu, B, H, Sq, Skv, D, cuts, masked):
+    import context_attention_diffusion_amd as cp
+    seed = 8000 + Sq + Skv + D
+    q = _rand_bits((B, Sq, H, D), seed)
+    k = _rand_bits((B, Skv, H, D), seed + 1)
+    v = _rand_bits((B, Skv, H, D), seed + 2)
+    mask = None
+    if masked:
+        mask = (np.random.default_rng(seed + 3).random((B, Skv)) > 0.4).astype(np.uint8)
+        mask[:, -1] = 1
+    edges = [0, *cuts, Skv]
+    print(f"[attn] partial+merge B={B} H={H} Sq={Sq} Skv={Skv} D={D} cuts={cuts} masked={masked}", flush=True)
+    qd = gu.to_dev(q)
+    o_parts, lses = _partials(cp, qd, k, v, mask, edges)
+    merged = cp.cp_attn_merge(o_parts, lses)
+    torch.cuda.synchronize()
+    qf, kf, vf = bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v)
+    got_p = o_parts.double().cpu().numpy()
+    got_l = lses.double().cpu().numpy()
+    for n, (a, b) in enumerate(zip(edges[:-1], edges[1:])):
+        mk = None if mask is None else mask[:, a:b]
+        ref_o, ref_l = OA.attention_partial(qf, kf[:, a:b], vf[:, a:b], mk)
+        _assert_close(got_p[n], ref_o, f"partial {n}")
+        fin = np.isfinite(ref_l)
+        assert np.array_equal(np.isfinite(got_l[n]), fin), "lse -inf pattern differs"
+        assert np.all(got_p[n][~np.repeat(fin.transpose(0, 2, 1)[..., None], D, axis=3)] == 0)
+        lerr = np.abs(got_l[n][fin] - ref_l[fin]).max() if fin.any() else 0.0
+        print(f"  lse {n}: max|err| {lerr:.3e}", flush=True)
+        assert lerr <= LSE_ERR
+    _assert_close(gu.to_f64(merged), OA.attention(qf, kf, vf, mask), "merged")
+
+
+def test_chunked_kv_arrival_full_size_sampled(gu):
+    """Image CP4 share with the gathered K/V arriving in four chunks of one rank's rows."""
+    import context_attention_diffusion_amd as cp
+    wl = workloads.WORKLOADS["image_cp4"]
+    q, k, v = workloads.global_qkv(wl)
+    q = np.ascontiguousarray(q[:, :wl.attn_rows])
+    Sl = wl.S_local
+    edges = [r * Sl for r in range(wl.W + 1)]
+    print("[attn] chunked K/V image_cp4", flush=True)
+    qd = gu.to_dev(q)
+    o_parts, lses = _partials(cp, qd, k, v, None, edges)
+    merged = cp.cp_attn_merge(o_parts, lses)
+    dense = cp.cp_attn_localq_globalkv(qd, gu.to_dev(k), gu.to_dev(v))
+    torch.cuda.synchronize()
+    got, whole = gu.to_f64(merged), gu.to_f64(dense)
+    assert np.abs(got - whole).max() <= 2e-2
+    rng = np.random.default_rng(wl.seed + 11)
+    rows = [(0, int(rng.integers(wl.attn_rows)), int(rng.integers(wl.H))) for _ in range(32)]
+    ref = OA.attention_rows(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), rows)
+    _assert_close(np.stack([got[b, i, h] for b, i, h in rows]), ref, "chunked image_cp4 sampled")

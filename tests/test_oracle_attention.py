@@ -227,6 +227,59 @@ def test_ulysses_attention_ranks_reassemble_full_attention(W, masked):
                                        rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("masked", [False, True])
+@pytest.mark.parametrize("cuts", [(7,), (1, 20), (5, 6, 30)])
+def test_chunked_keys_merge_to_full_attention(masked, cuts):
+    # attention over disjoint key chunks, merged by their log-sum-exp, is attention
+    # over all keys; the lse of the whole equals the logsumexp of the chunks' lses
+    B, Sq, Skv, H, D = 2, 9, 33, 2, 8
+    q, k, v = _rand((B, Sq, H, D), 50), _rand((B, Skv, H, D), 51), _rand((B, Skv, H, D), 52)
+    m = _mask(B, Skv, 53) if masked else None
+    edges = [0, *cuts, Skv]
+    parts = [A.attention_partial(q, k[:, a:b], v[:, a:b], None if m is None else m[:, a:b])
+             for a, b in zip(edges[:-1], edges[1:])]
+    o = A.merge_partials(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    np.testing.assert_allclose(o, A.attention(q, k, v, m), rtol=1e-12, atol=1e-13)
+    _, lse_all = A.attention_partial(q, k, v, m)
+    lses = np.stack([p[1] for p in parts])
+    np.testing.assert_allclose(lse_all, np.logaddexp.reduce(lses, axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_partial_lse_closed_forms():
+    # Q = 0: every z = 0, so lse = ln(number of valid keys); one valid key: lse = its z
+    B, Sq, Skv, H, D = 2, 3, 10, 1, 4
+    k, v = _rand((B, Skv, H, D), 54), _rand((B, Skv, H, D), 55)
+    m = np.ones((B, Skv), dtype=np.uint8)
+    m[0, 4:] = 0
+    _, lse = A.attention_partial(np.zeros((B, Sq, H, D)), k, v, m)
+    np.testing.assert_allclose(lse[0], math.log(4), rtol=1e-14)
+    np.testing.assert_allclose(lse[1], math.log(10), rtol=1e-14)
+    q = _rand((B, Sq, H, D), 56)
+    one = np.zeros((B, Skv), dtype=np.uint8)
+    one[:, 6] = 1
+    o, lse = A.attention_partial(q, k, v, one, scale=0.3)
+    for b in range(B):
+        for i in range(Sq):
+            assert lse[b, 0, i] == pytest.approx(0.3 * float(q[b, i, 0] @ k[b, 6, 0]), rel=1e-13)
+            np.testing.assert_allclose(o[b, i, 0], v[b, 6, 0], rtol=1e-14)
+
+
+def test_partial_fully_masked_rows_and_merge():
+    # a chunk with no valid key has lse = -inf and zero output, and the merge gives it
+    # no weight; with no valid key in any chunk the merged row is zero
+    B, Sq, Skv, H, D = 2, 2, 8, 1, 4
+    q, k, v = _rand((B, Sq, H, D), 57), _rand((B, Skv, H, D), 58), _rand((B, Skv, H, D), 59)
+    m = np.ones((B, Skv), dtype=np.uint8)
+    m[0, :4] = 0
+    m[1, :] = 0
+    p1 = A.attention_partial(q, k[:, :4], v[:, :4], m[:, :4])
+    p2 = A.attention_partial(q, k[:, 4:], v[:, 4:], m[:, 4:])
+    assert np.all(p1[1][0] == -np.inf) and np.all(p1[0][0] == 0)
+    o = A.merge_partials(np.stack([p1[0], p2[0]]), np.stack([p1[1], p2[1]]))
+    np.testing.assert_allclose(o[0], p2[0][0], rtol=1e-14)
+    assert np.all(o[1] == 0)
+
+
 def test_bf16_widening_is_exact():
     bits = np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0x4049, 0x7F80, 0x0001, 0x7F7F],
                     dtype=np.uint16)

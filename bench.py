@@ -75,6 +75,10 @@ def parse():
     p.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench and of "
                         "--calib-copy into a traffic summary; no GPU work")
+    p.add_argument("--uaa", action="store_true",
+                   help="per-rank comparison of head padding (usp4+uaa) and the composed U2xA2 "
+                        "layout at heads 14, D 128; prints its own JSON line")
+    p.add_argument("--uaa-seqs", default="16384,32768,65536")
     p.add_argument("--only", default=None,
                    help="profile aid: run only this kernel's launches in the timed loop "
                         "(pack|unpack|attn|merge); the JSON line is then not the headline")
@@ -474,6 +478,124 @@ def chunked_kv(path, burst=10):
     return res
 
 
+def uaa_compare(seqs, heads=14, D=128, seed=1240):
+    """Per-rank comparison of a padded Ulysses layout against the composed one, at the
+    shapes of the pages' attention benchmark (heads 14, D 128, four ranks):
+
+    usp4+uaa: Ulysses over 4 ranks; 14 heads padded to 16 (4 per rank).  Step: padded
+              pack -> exchange -> unpack -> attention of 4 heads over all S rows -> send
+              (identity, B = 1) -> exchange -> merge dropping the padding heads.  Also
+              timed with the fused attention (recv -> send).
+    cp2usp2:  Ulysses 2 x AllGather-KV 2; 7 heads per rank, S/2 query rows against the
+              gathered S keys.  Step: pack -> exchange -> unpack (K/V into region 0 of the
+              gathered K/V; region 1, the other AllGather rank's share, is resident) ->
+              attention -> send -> exchange -> merge.
+    Inputs are seeded N(0, 1) bf16 drawn on the GPU; every exchange partner's buffer is
+    resident before timing.  Returns one record per sequence length."""
+    import torch
+    import context_attention_diffusion_amd as cp
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+
+    def randn(*shape):
+        return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    res = []
+    for S in seqs:
+        rec = {"S": S}
+        scale = 1.0 / math.sqrt(D)
+        # ---- usp4 + uaa
+        W, Sl = 4, S // 4
+        H_pad = -(-heads // W) * W
+        Hl = H_pad // W
+        x = [randn(1, Sl, heads, D) for _ in range(3)]
+        st = [torch.empty((W, Sl, Hl, 3 * D), dtype=torch.bfloat16, device=dev) for _ in range(W)]
+        for r in range(1, W):
+            cp.cp_pack_qkv_dst_major_padded(*[randn(1, Sl, heads, D) for _ in range(3)], W, H_pad, staging=st[r])
+        recv = torch.empty_like(st[0])
+        hs = [torch.empty((1, S, Hl, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+        o = torch.empty((1, S, Hl, D), dtype=torch.bfloat16, device=dev)
+        snd_f = torch.empty((W, 1, Sl, Hl, D), dtype=torch.bfloat16, device=dev)
+        peers = [None] + [randn(W, 1, Sl, Hl, D) for _ in range(W - 1)]
+        rcv = torch.empty((W, 1, Sl, Hl, D), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((1, Sl, heads, D), dtype=torch.bfloat16, device=dev)
+
+        def u_front():
+            cp.cp_pack_qkv_dst_major_padded(*x, W, H_pad, staging=st[0])
+            cp.cp_sim_exchange(st, 0, recv=recv)
+
+        def u_attn():
+            cp.cp_attn_localq_globalkv(*hs, scale=scale, out=o)
+
+        def u_back(snd):
+            cp.cp_sim_exchange([snd] + peers[1:], 0, recv=rcv)
+            cp.cp_output_merge_cropped(rcv, heads, out=out)
+
+        def u_step():
+            u_front()
+            cp.cp_unpack_head_sharded(recv, 1, W, out=hs)
+            u_attn()
+            u_back(o.view(W, 1, Sl, Hl, D))
+
+        def u_fused_step():
+            u_front()
+            cp.cp_attn_recv_to_send(recv, 1, W, scale=scale, out=snd_f)
+            u_back(snd_f)
+
+        u_step()
+        u_fused_step()
+        torch.cuda.synchronize()
+        burst = 3 if S > 40000 else 5
+        rec["uaa_usp4"] = {"heads_per_rank": Hl, "padded_heads": H_pad - heads,
+                           "attn_us": time_burst(u_attn, burst) * 1e3,
+                           "step_us": time_burst(u_step, burst) * 1e3,
+                           "fused_step_us": time_burst(u_fused_step, burst) * 1e3,
+                           "attn_flops": 4 * Hl * S * S * D}
+        del x, st, recv, hs, o, snd_f, peers, rcv, out
+        # ---- cp2usp2: Ulysses 2 inside an AllGather-KV pair
+        U = 2
+        Hu = heads // U
+        x = [randn(1, Sl, heads, D) for _ in range(3)]
+        st = [torch.empty((U, Sl, Hu, 3 * D), dtype=torch.bfloat16, device=dev) for _ in range(U)]
+        cp.cp_pack_qkv_dst_major(*[randn(1, Sl, heads, D) for _ in range(3)], U, staging=st[1])
+        recv = torch.empty_like(st[0])
+        q_hs = torch.empty((1, U * Sl, Hu, D), dtype=torch.bfloat16, device=dev)
+        k_glob, v_glob = randn(1, S, Hu, D), randn(1, S, Hu, D)
+        k_reg0, v_reg0 = k_glob[:, :U * Sl], v_glob[:, :U * Sl]
+        o = torch.empty((1, U * Sl, Hu, D), dtype=torch.bfloat16, device=dev)
+        peers = [None, randn(U, 1, Sl, Hu, D)]
+        rcv = torch.empty((U, 1, Sl, Hu, D), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((1, Sl, heads, D), dtype=torch.bfloat16, device=dev)
+
+        def c_attn():
+            cp.cp_attn_localq_globalkv(q_hs, k_glob, v_glob, scale=scale, out=o)
+
+        def c_step():
+            cp.cp_pack_qkv_dst_major(*x, U, staging=st[0])
+            cp.cp_sim_exchange(st, 0, recv=recv)
+            cp.cp_unpack_head_sharded(recv, 1, U, out=(q_hs, k_reg0, v_reg0))
+            c_attn()
+            cp.cp_sim_exchange([o.view(U, 1, Sl, Hu, D)] + peers[1:], 0, recv=rcv)
+            cp.cp_output_reverse(1, rcv, U, 1, out=out)
+
+        c_step()
+        torch.cuda.synchronize()
+        rec["cp2usp2"] = {"heads_per_rank": Hu, "attn_us": time_burst(c_attn, burst) * 1e3,
+                          "step_us": time_burst(c_step, burst) * 1e3,
+                          "attn_flops": 4 * Hu * (S // 2) * S * D}
+        del x, st, recv, q_hs, k_glob, v_glob, k_reg0, v_reg0, o, peers, rcv, out
+        torch.cuda.empty_cache()
+        u, c = rec["uaa_usp4"], rec["cp2usp2"]
+        rec["attn_reduction"] = 1.0 - c["attn_us"] / u["attn_us"]
+        rec["step_reduction"] = 1.0 - c["step_us"] / u["step_us"]
+        rec["attn_TFLOPs"] = {"uaa_usp4": u["attn_flops"] / (u["attn_us"] * 1e-6) / 1e12,
+                              "cp2usp2": c["attn_flops"] / (c["attn_us"] * 1e-6) / 1e12}
+        res.append(rec)
+    return res
+
+
 ATTN_SRC = os.path.join(ROOT, "context_attention_diffusion_amd", "csrc", "cp_attention.hip")
 CALIB_BYTES = 256 << 20
 
@@ -541,6 +663,15 @@ def main():
 
     if args.calib_copy:
         calib_copy()
+        return
+    if args.uaa:
+        seqs = [int(x) for x in args.uaa_seqs.split(",")]
+        recs = uaa_compare(seqs)
+        print(json.dumps({"metric": "per-rank attention and step time, UAA head padding (usp4) vs "
+                                    "composed Ulysses 2 x AllGather-KV 2; heads 14, D 128",
+                          "unit": "us", "higher_is_better": False, "n_gpus": 1, "dtype": "bf16",
+                          "data": "synthetic", "records": recs,
+                          "ideal_attn_reduction": 1.0 - 3.5 / 4.0}), flush=True)
         return
 
     import workloads

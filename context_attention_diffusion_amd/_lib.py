@@ -32,6 +32,10 @@ SIGNATURES = {
                                                   _i64, ctypes.c_float, ctypes.c_int, _vp,
                                                   ctypes.c_size_t, _vp]),
     "cp_attn_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64]),
+    "cp_pack_qkv_dst_major_padded": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                                    _i64, ctypes.c_int, _vp]),
+    "cp_output_merge_cropped": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                               ctypes.c_int, _vp]),
     "cp_attn_partial": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                        ctypes.c_float, ctypes.c_int, _vp]),
     "cp_attn_merge": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]),
@@ -55,7 +59,7 @@ CP_ERR_WORKSPACE = 11
 
 CP_DTYPE_BF16 = 0
 CP_DTYPE_FP16 = 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _lib = None
 

@@ -47,6 +47,8 @@ __device__ __forceinline__ void st(vec_t* p, vec_t v) {
 // m.src(o) / m.dst(o) for output-ordered index o.  Blocks stride over tiles of
 // kVecPerBlock vectors; each thread loads its 4 vectors of the next tile before
 // storing those of the current one, so reads and writes stay in flight together.
+// A map with kZeroFill set may return nullptr from src(o): that output vector is
+// zero (padding).
 template <class Map, bool NT_STORE>
 __global__ void __launch_bounds__(kThreads) permute_kernel(Map m, uint32_t n_vec) {
   const uint32_t n_tiles = (n_vec + kVecPerBlock - 1) / kVecPerBlock;
@@ -57,7 +59,14 @@ __global__ void __launch_bounds__(kThreads) permute_kernel(Map m, uint32_t n_vec
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
       const uint32_t o = t * kVecPerBlock + u * kThreads + threadIdx.x;
-      if (o < n_vec) buf[u] = ld(m.src(o));
+      if (o < n_vec) {
+        if constexpr (Map::kZeroFill) {
+          const vec_t* p = m.src(o);
+          buf[u] = p ? ld(p) : vec_t{0u, 0u, 0u, 0u};
+        } else {
+          buf[u] = ld(m.src(o));
+        }
+      }
     }
   };
   auto store = [&](uint32_t t, const vec_t* buf) {
@@ -86,6 +95,7 @@ template <int VD>
 struct PackMap {
   // the staging buffer goes to the collective, not to another kernel on this GPU
   static constexpr bool kNontemporalStore = true;
+  static constexpr bool kZeroFill = false;
   const vec_t *q, *k, *v;
   vec_t* out;
   uint32_t vd, H_local, H;
@@ -111,6 +121,7 @@ template <int VD>
 struct UnpackMap {
   // Q/K/V are read next (K/V many times) by the attention kernel: keep them cacheable
   static constexpr bool kNontemporalStore = false;
+  static constexpr bool kZeroFill = false;
   const vec_t* recv;
   vec_t *q, *k, *v;
   uint32_t vd, H_local, wsl;                  // wsl = W * S_local output rows per batch
@@ -135,6 +146,7 @@ struct UnpackMap {
 template <int PHASE>
 struct ReverseMap {
   static constexpr bool kNontemporalStore = PHASE == 0;  // send layout goes to the collective
+  static constexpr bool kZeroFill = false;
   const vec_t* src_;
   vec_t* out;
   uint32_t W, B, S_local;
@@ -159,10 +171,58 @@ struct ReverseMap {
   __device__ __forceinline__ vec_t* dst(uint32_t o) const { return out + o; }
 };
 
+// pack with head padding: as PackMap over H_pad = W * H_local heads, of which
+// heads >= H (the source's head count and row stride) are zeros.
+template <int VD>
+struct PackPadMap {
+  static constexpr bool kNontemporalStore = true;
+  static constexpr bool kZeroFill = true;
+  const vec_t *q, *k, *v;
+  vec_t* out;
+  uint32_t vd, H_local, H;
+  FastDiv div_vd, div_hl, div_rows;
+  __device__ __forceinline__ const vec_t* src(uint32_t o) const {
+    uint32_t t, dv;
+    if (VD > 0) { dv = o % VD; t = o / VD; } else { div_vd.divmod(o, t, dv); }
+    const uint32_t c = t % 3u;
+    t /= 3u;
+    uint32_t rj, hl, j, row;
+    div_hl.divmod(t, rj, hl);
+    div_rows.divmod(rj, j, row);
+    const uint32_t g = j * H_local + hl;
+    if (g >= H) return nullptr;
+    const vec_t* base = c == 0 ? q : (c == 1 ? k : v);
+    const uint32_t w = VD > 0 ? uint32_t(VD) : vd;
+    return base + (size_t(row) * H + g) * w + dv;
+  }
+  __device__ __forceinline__ vec_t* dst(uint32_t o) const { return out + o; }
+};
+
+// merge with the padded heads dropped: output order (b, s, g, dv) over the H
+// real heads; head g = j * H_local + hl comes from rank j's chunk.
+struct MergeCropMap {
+  static constexpr bool kNontemporalStore = false;
+  static constexpr bool kZeroFill = false;
+  const vec_t* src_;
+  vec_t* out;
+  uint32_t B, S_local, H_local;
+  FastDiv div_vd, div_h, div_hl;
+  __device__ __forceinline__ const vec_t* src(uint32_t o) const {
+    uint32_t t, dv, bs, g, j, hl;
+    div_vd.divmod(o, t, dv);
+    div_h.divmod(t, bs, g);
+    div_hl.divmod(g, j, hl);
+    // [W][B][S_local][H_local][D]: rank j's chunk holds B * S_local rows
+    return src_ + ((size_t(j) * B * S_local + bs) * H_local + hl) * div_vd.d + dv;
+  }
+  __device__ __forceinline__ vec_t* dst(uint32_t o) const { return out + o; }
+};
+
 // simulated exchange: recv chunk r <- chunk `rank` of sends[r].
 constexpr int kMaxRanks = 64;
 struct ExchangeMap {
   static constexpr bool kNontemporalStore = false;  // the receive buffer is unpacked next
+  static constexpr bool kZeroFill = false;
   const vec_t* p[kMaxRanks];
   vec_t* recv;
   uint32_t rank;
@@ -234,6 +294,61 @@ extern "C" int cp_pack_qkv_dst_major(const void* q, const void* k, const void* v
                           uint32_t(n_vec), s);
   return launch_permute(PackMap<0>{qv, kv, vv, out, vd, H_local, uint32_t(H), dvd, dhl, drows},
                         uint32_t(n_vec), s);
+}
+
+extern "C" int cp_pack_qkv_dst_major_padded(const void* q, const void* k, const void* v, void* staging,
+                                            int64_t B, int64_t S_local, int64_t H, int64_t H_pad, int64_t D,
+                                            int64_t W, int dtype, cp_stream_t stream) {
+  if (!q || !k || !v || !staging) return CP_ERR_NULL;
+  int st = check_layout_dims(B, S_local, H, D, W, dtype);
+  if (st) return st;
+  if (H_pad < H) return CP_ERR_SHAPE;
+  if (H_pad % W != 0) return CP_ERR_DIVISIBILITY;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(staging))
+    return CP_ERR_ALIGNMENT;
+  int64_t rows, per_in, per_out, n_vec;
+  if (!mul_capped(B, S_local, kMaxVectors, &rows) || !mul_capped(rows, H * (D / 8), kMaxVectors, &per_in) ||
+      !mul_capped(rows, H_pad * (D / 8), kMaxVectors, &per_out) ||
+      !mul_capped(per_out, 3, kMaxVectors, &n_vec))
+    return CP_ERR_SHAPE;
+  const size_t ib = size_t(per_in) * 16, sb = size_t(n_vec) * 16;
+  if (overlaps(staging, sb, q, ib) || overlaps(staging, sb, k, ib) || overlaps(staging, sb, v, ib))
+    return CP_ERR_ALIAS;
+  const uint32_t H_local = uint32_t(H_pad / W);
+  const uint32_t vd = uint32_t(D / 8);
+  FastDiv dvd{vd}, dhl{H_local}, drows{uint32_t(rows)};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const auto* qv = static_cast<const vec_t*>(q);
+  const auto* kv = static_cast<const vec_t*>(k);
+  const auto* vv = static_cast<const vec_t*>(v);
+  auto* out = static_cast<vec_t*>(staging);
+  if (vd == 16)
+    return launch_permute(PackPadMap<16>{qv, kv, vv, out, vd, H_local, uint32_t(H), dvd, dhl, drows},
+                          uint32_t(n_vec), s);
+  if (vd == 8)
+    return launch_permute(PackPadMap<8>{qv, kv, vv, out, vd, H_local, uint32_t(H), dvd, dhl, drows},
+                          uint32_t(n_vec), s);
+  return launch_permute(PackPadMap<0>{qv, kv, vv, out, vd, H_local, uint32_t(H), dvd, dhl, drows},
+                        uint32_t(n_vec), s);
+}
+
+extern "C" int cp_output_merge_cropped(const void* src, void* dst, int64_t B, int64_t S_local, int64_t H_local,
+                                       int64_t H, int64_t D, int64_t W, int dtype, cp_stream_t stream) {
+  if (!src || !dst) return CP_ERR_NULL;
+  int st = check_layout_dims(B, S_local, H_local, D, W, dtype);
+  if (st) return st;
+  if (H < 1 || H > W * H_local) return CP_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return CP_ERR_ALIGNMENT;
+  int64_t rows, in_vec, n_vec;
+  if (!mul_capped(B, S_local, kMaxVectors, &rows) ||
+      !mul_capped(rows, W * H_local * (D / 8), kMaxVectors, &in_vec) ||
+      !mul_capped(rows, H * (D / 8), kMaxVectors, &n_vec))
+    return CP_ERR_SHAPE;
+  if (overlaps(src, size_t(in_vec) * 16, dst, size_t(n_vec) * 16)) return CP_ERR_ALIAS;
+  const uint32_t vd = uint32_t(D / 8);
+  MergeCropMap m{static_cast<const vec_t*>(src), static_cast<vec_t*>(dst), uint32_t(B), uint32_t(S_local),
+                 uint32_t(H_local), FastDiv(vd), FastDiv(uint32_t(H)), FastDiv(uint32_t(H_local))};
+  return launch_permute(m, uint32_t(n_vec), reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int cp_unpack_head_sharded(const void* recv, void* q_out, void* k_out, void* v_out,

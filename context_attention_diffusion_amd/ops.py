@@ -93,6 +93,41 @@ def cp_pack_qkv_dst_major(q, k, v, W: int, staging=None, stream=None) -> torch.T
     return staging
 
 
+def cp_pack_qkv_dst_major_padded(q, k, v, W: int, H_pad: int, staging=None, stream=None) -> torch.Tensor:
+    """[B,S_l,H,D] x3 -> staging [W, B*S_l, H_pad/W, 3D], heads >= H zero (head padding)."""
+    lib = _lib.load()
+    B, Sl, H, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    if H_pad < H or H_pad % W:
+        raise ValueError("H_pad must be >= H and divide by W")
+    shape = (W, B * Sl, H_pad // W, 3 * D)
+    if staging is None:
+        staging = staging_buffer("cp_pack_send", shape, q.dtype, q.device)
+    if tuple(staging.shape) != shape or staging.dtype != q.dtype:
+        raise ValueError(f"staging must be {shape} {q.dtype}")
+    _lib.check("cp_pack_qkv_dst_major_padded", lib.cp_pack_qkv_dst_major_padded(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(staging, "staging"),
+        B, Sl, H, H_pad, D, W, _dtype_code(q), _stream(stream)))
+    return staging
+
+
+def cp_output_merge_cropped(src, H: int, out=None, stream=None) -> torch.Tensor:
+    """[W, B, S_l, H_l, D] -> [B, S_l, H, D]: the merge keeping the first H of W*H_l heads."""
+    lib = _lib.load()
+    W, B, Sl, Hl, D = src.shape
+    if not 1 <= H <= W * Hl:
+        raise ValueError("H must be in [1, W*H_l]")
+    shape = (B, Sl, H, D)
+    if out is None:
+        out = torch.empty(shape, dtype=src.dtype, device=src.device)
+    if tuple(out.shape) != shape or out.dtype != src.dtype:
+        raise ValueError(f"out must be {shape} {src.dtype}")
+    _lib.check("cp_output_merge_cropped", lib.cp_output_merge_cropped(
+        _dev(src, "src"), _dev(out, "dst"), B, Sl, Hl, H, D, W, _dtype_code(src), _stream(stream)))
+    return out
+
+
 def cp_sim_exchange(sends, rank: int, recv=None, stream=None) -> torch.Tensor:
     """Single-GPU stand-in for the all-to-all: ``recv`` chunk r = chunk ``rank`` of ``sends[r]``."""
     lib = _lib.load()

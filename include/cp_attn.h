@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CP_ABI_VERSION 4
+#define CP_ABI_VERSION 5
 
 typedef struct ihipStream_t* cp_stream_t; /* == hipStream_t */
 
@@ -97,6 +97,39 @@ const char* cp_status_string(int status);
 int cp_pack_qkv_dst_major(const void* q, const void* k, const void* v, void* staging,
                           int64_t B, int64_t S_local, int64_t H, int64_t D, int64_t W,
                           int dtype, cp_stream_t stream);
+
+/*
+ * Destination-major pack with head padding, for head counts that the Ulysses
+ * degree does not divide (the UAA padding of [vllm-omni#7641]'s attention
+ * benchmark: 14 heads over 4 ranks padded to 16, +14.3% attention work).  The
+ * head axis is read as padded with zero heads up to H_pad, then packed as by
+ * cp_pack_qkv_dst_major:
+ *
+ *   staging[j][b*S_local+s][hl][c*D+d] = X_c[b][s][j*H_local+hl][d]  if j*H_local+hl < H,
+ *                                        0                            otherwise,
+ *   H_local = H_pad / W.
+ *
+ *   q, k, v : [B][S_local][H][D];  staging : [W][B*S_local][H_pad/W][3*D]
+ *
+ * Requires H <= H_pad, H_pad % W == 0 (CP_ERR_DIVISIBILITY), and the conditions
+ * of cp_pack_qkv_dst_major.  H_pad == H is the plain pack.
+ */
+int cp_pack_qkv_dst_major_padded(const void* q, const void* k, const void* v, void* staging,
+                                 int64_t B, int64_t S_local, int64_t H, int64_t H_pad, int64_t D,
+                                 int64_t W, int dtype, cp_stream_t stream);
+
+/*
+ * Output merge of a padded Ulysses layout: as cp_output_reverse phase 1, keeping
+ * only the first H of the W*H_local heads (the padding heads are dropped):
+ *
+ *   dst[b][s][g][d] = src[g / H_local][b][s][g % H_local][d],  g < H.
+ *
+ *   src : [W][B][S_local][H_local][D];  dst : [B][S_local][H][D]
+ *
+ * Requires 1 <= H <= W*H_local and the conditions of cp_output_reverse.
+ */
+int cp_output_merge_cropped(const void* src, void* dst, int64_t B, int64_t S_local, int64_t H_local,
+                            int64_t H, int64_t D, int64_t W, int dtype, cp_stream_t stream);
 
 /*
  * Simulated W-way all-to-all, receive side of one rank (the single-GPU stand-in

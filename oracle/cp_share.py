@@ -113,3 +113,21 @@ def ulysses_attention_all(q_full, k_full, v_full, W, key_mask=None, scale=None):
     snd = [ulysses_attention_send(recv[j], B, W, key_mask, scale) for j in range(W)]
     rcv = _layout.exchange(snd)
     return recv, [_layout.output_reverse_merge(x) for x in rcv]
+
+
+def uaa_attention_all(q_full, k_full, v_full, W, key_mask=None, scale=None):
+    """Every rank of a Ulysses group whose degree W does not divide the head count:
+    zero heads pad H up to a multiple of W before the pack, each rank attends its
+    padded head slice, and the merge drops the padding.  Returns
+    ``(per-rank attention inputs, per-rank outputs [B, S_l, H, D])``."""
+    B, S, H, D = q_full.shape
+    if S % W:
+        raise ValueError("S must divide by W")
+    H_pad = -(-H // W) * W
+    Sl = S // W
+    shards = [tuple(t[:, r * Sl:(r + 1) * Sl] for t in (q_full, k_full, v_full)) for r in range(W)]
+    recv = _layout.exchange([_layout.pack_qkv_dst_major_padded(*shards[r], W, H_pad) for r in range(W)])
+    ins = [_layout.unpack_head_sharded(recv[j], B, W) for j in range(W)]
+    outs = [_attn.attention(q, k, v, key_mask=key_mask, scale=scale) for q, k, v in ins]
+    rcv = _layout.exchange([_layout.output_reverse_send(o, W) for o in outs])
+    return ins, [_layout.output_merge_cropped(x, H) for x in rcv]

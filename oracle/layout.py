@@ -187,6 +187,28 @@ def output_reverse_merge_loops(rcv):
     return out
 
 
+# ------------------------------------------------------------------ head padding
+#
+# Head counts the Ulysses degree does not divide ([vllm-omni#7641], attention
+# benchmark: 14 heads over 4 ranks run as 16, "+14.3% attention work"): the head
+# axis is padded with zero heads to a multiple of W before the pack, and the
+# padding heads are dropped after the merge.
+
+
+def pack_qkv_dst_major_padded(q, k, v, W, H_pad):
+    """Pack of Q/K/V whose head axis is first padded with zero heads up to ``H_pad``."""
+    H = q.shape[2]
+    if H_pad < H or H_pad % W:
+        raise ValueError("H_pad must be >= H and divide by W")
+    pad = [(0, 0), (0, 0), (0, H_pad - H), (0, 0)]
+    return pack_qkv_dst_major(*(np.pad(t, pad) for t in (q, k, v)), W)
+
+
+def output_merge_cropped(rcv, H):
+    """Merge of the received output chunks, keeping the first ``H`` heads."""
+    return output_reverse_merge(rcv)[:, :, :H, :]
+
+
 # --------------------------------------------------------------------------- composed
 
 def ulysses_forward(shards, W):

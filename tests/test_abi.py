@@ -71,6 +71,21 @@ def _pack(**kw):
                                              a["H"], a["D"], a["W"], a["dtype"], None)
 
 
+def _pack_pad(**kw):
+    a = dict(q=A, k=A + BIG, v=A + 2 * BIG, st=A + 3 * BIG, B=1, Sl=4, H=14, Hp=16, D=128, W=4,
+             dtype=BF16)
+    a.update(kw)
+    return _lib.load().cp_pack_qkv_dst_major_padded(a["q"], a["k"], a["v"], a["st"], a["B"], a["Sl"],
+                                                    a["H"], a["Hp"], a["D"], a["W"], a["dtype"], None)
+
+
+def _merge_crop(**kw):
+    a = dict(s=A, d=A + BIG, B=1, Sl=4, Hl=4, H=14, D=128, W=4, dtype=BF16)
+    a.update(kw)
+    return _lib.load().cp_output_merge_cropped(a["s"], a["d"], a["B"], a["Sl"], a["Hl"], a["H"], a["D"],
+                                               a["W"], a["dtype"], None)
+
+
 def _unpack(**kw):
     a = dict(r=A, q=A + BIG, k=A + 2 * BIG, v=A + 3 * BIG, B=1, Sl=4, Hl=2, D=128, W=2,
              dtype=BF16)
@@ -260,6 +275,34 @@ def test_partial_rejects(kw, code):
 ])
 def test_merge_rejects(kw, code):
     assert _merge(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.CP_ERR_NULL),
+    (dict(dtype=5), _lib.CP_ERR_DTYPE),
+    (dict(Hp=13), _lib.CP_ERR_SHAPE),               # H_pad < H
+    (dict(Hp=18), _lib.CP_ERR_DIVISIBILITY),        # 18 % 4
+    (dict(D=12), _lib.CP_ERR_HEAD_DIM),
+    (dict(st=A + 3 * BIG + 8), _lib.CP_ERR_ALIGNMENT),
+    (dict(st=A + 16), _lib.CP_ERR_ALIAS),           # staging overlaps q
+    (dict(B=1 << 20, Sl=1 << 20), _lib.CP_ERR_SHAPE),
+])
+def test_pack_padded_rejects(kw, code):
+    assert _pack_pad(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=None), _lib.CP_ERR_NULL),
+    (dict(H=17), _lib.CP_ERR_SHAPE),                # more heads than W * H_local
+    (dict(H=0), _lib.CP_ERR_SHAPE),
+    (dict(D=4), _lib.CP_ERR_HEAD_DIM),
+    (dict(s=A + 4), _lib.CP_ERR_ALIGNMENT),
+    (dict(d=A + 1024), _lib.CP_ERR_ALIAS),
+])
+def test_merge_cropped_rejects(kw, code):
+    assert _merge_crop(**kw) == code
 
 
 def test_workspace_bytes():

@@ -41,11 +41,13 @@ def _check_group(gu, full, W, dtype=torch.bfloat16):
             np.testing.assert_array_equal(got, full[c][:, :, r * Hl:(r + 1) * Hl],
                                           err_msg=f"spec rank {r} c {c}")
             assert outs[r][c].is_contiguous()
-    # Output reverse on each head-sharded tensor: oracle parity and round trip.
+    # Output reverse on each head-sharded tensor: oracle parity and round trip (the
+    # oracle reverses its own unpacked tensors).
+    o_outs = [L.unpack_head_sharded(o_recv[r], B, W) for r in range(W)]
     for c in range(3):
         o_hs = [outs[r][c] for r in range(W)]
         snd, rcv, merged = gu.reverse_all_ranks(o_hs, W, B)
-        o_snd = [L.output_reverse_send(gu.to_bits(x), W) for x in o_hs]
+        o_snd = [L.output_reverse_send(o_outs[r][c], W) for r in range(W)]
         o_rcv = L.exchange(o_snd)
         for r in range(W):
             np.testing.assert_array_equal(gu.to_bits(snd[r]), o_snd[r], err_msg=f"send r{r} c{c}")
@@ -124,3 +126,37 @@ def test_unpack_into_gathered_kv_slice(gu):
     got = gu.to_bits(kg)
     np.testing.assert_array_equal(got[:, W * Sl:], full[1][:, :, :H // W])
     assert (got[:, :W * Sl] == 0).all()
+
+
+@pytest.mark.parametrize("W,B,S,H,D", [(4, 1, 64, 14, 128), (4, 2, 24, 6, 64), (3, 1, 30, 4, 8), (8, 1, 64, 12, 128)])
+def test_padded_pack_and_cropped_merge(gu, W, B, S, H, D):
+    """Head padding (H % W != 0): padded pack -> exchange -> unpack, then the reverse
+    with the cropped merge, every buffer bit-exact against the oracle."""
+    import context_attention_diffusion_amd as cp
+    rng = np.random.default_rng(W * 1000 + H * 10 + D)
+    full = [rng.integers(1, 65535, size=(B, S, H, D)).astype(np.uint16) for _ in range(3)]
+    H_pad = -(-H // W) * W
+    Hl, Sl = H_pad // W, S // W
+    shards = [tuple(np.ascontiguousarray(t[:, r * Sl:(r + 1) * Sl]) for t in full) for r in range(W)]
+    print(f"[layout] padded W={W} B={B} S={S} H={H} H_pad={H_pad} D={D}", flush=True)
+    staging = [cp.cp_pack_qkv_dst_major_padded(*(gu.to_dev(x) for x in shards[r]), W, H_pad,
+                                               staging=torch.empty((W, B * Sl, Hl, 3 * D), dtype=torch.bfloat16,
+                                                                   device=gu.DEV)) for r in range(W)]
+    o_staging = [L.pack_qkv_dst_major_padded(*shards[r], W, H_pad) for r in range(W)]
+    recv = [cp.cp_sim_exchange(staging, j) for j in range(W)]
+    outs = [cp.cp_unpack_head_sharded(recv[j], B, W) for j in range(W)]
+    for r in range(W):
+        np.testing.assert_array_equal(gu.to_bits(staging[r]), o_staging[r], err_msg=f"padded pack rank {r}")
+    # reverse of the unpacked tensors, cropped merge: every rank's original shard;
+    # the oracle runs the same chain on its own buffers
+    o_recv = L.exchange(o_staging)
+    o_outs = [L.unpack_head_sharded(o_recv[j], B, W) for j in range(W)]
+    for c in range(3):
+        snd = [cp.cp_output_reverse(0, outs[j][c], W, B) for j in range(W)]
+        rcv = [cp.cp_sim_exchange(snd, r) for r in range(W)]
+        o_rcv = L.exchange([L.output_reverse_send(o_outs[j][c], W) for j in range(W)])
+        for r in range(W):
+            got = cp.cp_output_merge_cropped(rcv[r], H)
+            o_got = L.output_merge_cropped(o_rcv[r], H)
+            np.testing.assert_array_equal(gu.to_bits(got), o_got, err_msg=f"cropped merge rank {r} c {c}")
+            np.testing.assert_array_equal(gu.to_bits(got), shards[r][c], err_msg=f"round trip rank {r} c {c}")

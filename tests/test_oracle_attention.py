@@ -280,6 +280,18 @@ def test_partial_fully_masked_rows_and_merge():
     assert np.all(o[1] == 0)
 
 
+@pytest.mark.parametrize("W,H", [(4, 6), (4, 14), (3, 4)])
+def test_uaa_padded_ranks_reassemble_full_attention(W, H):
+    # zero padding heads attend to zero keys and values; dropping them after the
+    # merge leaves every rank with its rows of full attention over the real heads
+    B, S, D = 1, 12, 4
+    q, k, v = _rand((B, S, H, D), 60), _rand((B, S, H, D), 61), _rand((B, S, H, D), 62)
+    ins, outs = cp_share.uaa_attention_all(q, k, v, W)
+    np.testing.assert_allclose(np.concatenate(outs, axis=1), A.attention(q, k, v), rtol=1e-12, atol=1e-13)
+    H_pad = -(-H // W) * W
+    assert sum(x[0].shape[2] for x in ins) == H_pad
+
+
 def test_bf16_widening_is_exact():
     bits = np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0x4049, 0x7F80, 0x0001, 0x7F7F],
                     dtype=np.uint16)

@@ -239,3 +239,60 @@ def test_layout_rejects_indivisible_shapes():
         layout.exchange([np.zeros(3), np.zeros(3)])
     with pytest.raises(ValueError):
         layout.output_reverse_send(np.zeros((1, 3, 1, 1)), 2)
+
+
+# ----------------------------------------------------------------- head padding
+
+def _pack_padded_loops(q, k, v, W, H_pad):
+    """The padded pack written element by element from its definition."""
+    B, Sl, H, D = q.shape
+    Hl = H_pad // W
+    out = np.zeros((W, B * Sl, Hl, 3 * D), dtype=q.dtype)
+    for j in range(W):
+        for b in range(B):
+            for s in range(Sl):
+                for hl in range(Hl):
+                    g = j * Hl + hl
+                    if g >= H:
+                        continue
+                    for c, t in enumerate((q, k, v)):
+                        for d in range(D):
+                            out[j, b * Sl + s, hl, c * D + d] = t[b, s, g, d]
+    return out
+
+
+@pytest.mark.parametrize("W,B,Sl,H,H_pad,D", [(4, 1, 3, 14, 16, 2), (3, 2, 2, 4, 6, 3), (2, 1, 2, 3, 4, 1)])
+def test_padded_pack_matches_loops(W, B, Sl, H, H_pad, D):
+    rng = np.random.default_rng(W * 100 + H)
+    q, k, v = (rng.integers(1, 65535, size=(B, Sl, H, D)).astype(np.uint16) for _ in range(3))
+    np.testing.assert_array_equal(layout.pack_qkv_dst_major_padded(q, k, v, W, H_pad),
+                                  _pack_padded_loops(q, k, v, W, H_pad))
+
+
+def test_padded_pack_without_padding_is_the_plain_pack():
+    rng = np.random.default_rng(3)
+    q, k, v = (rng.integers(0, 65535, size=(2, 3, 8, 4)).astype(np.uint16) for _ in range(3))
+    np.testing.assert_array_equal(layout.pack_qkv_dst_major_padded(q, k, v, 4, 8),
+                                  layout.pack_qkv_dst_major(q, k, v, 4))
+
+
+@pytest.mark.parametrize("W,B,S,H,D", [(4, 1, 16, 14, 4), (4, 2, 8, 6, 2), (3, 2, 12, 4, 3)])
+def test_padded_forward_spec_and_cropped_round_trip(W, B, S, H, D):
+    # After padded pack -> exchange -> unpack, rank j holds global heads
+    # [j*H_l, (j+1)*H_l) of the sequence-concatenated tensor, zeros past H; the
+    # reverse with the cropped merge returns every rank's original shard.
+    rng = np.random.default_rng(S + H)
+    full = [rng.integers(1, 65535, size=(B, S, H, D)).astype(np.uint16) for _ in range(3)]
+    H_pad = -(-H // W) * W
+    Hl, Sl = H_pad // W, S // W
+    shards = [tuple(t[:, r * Sl:(r + 1) * Sl] for t in full) for r in range(W)]
+    recv = layout.exchange([layout.pack_qkv_dst_major_padded(*sh, W, H_pad) for sh in shards])
+    outs = [layout.unpack_head_sharded(recv[j], B, W) for j in range(W)]
+    padded = [np.pad(t, [(0, 0), (0, 0), (0, H_pad - H), (0, 0)]) for t in full]
+    for j in range(W):
+        for c in range(3):
+            np.testing.assert_array_equal(outs[j][c], padded[c][:, :, j * Hl:(j + 1) * Hl])
+    for c in range(3):
+        rcv = layout.exchange([layout.output_reverse_send(outs[j][c], W) for j in range(W)])
+        for r in range(W):
+            np.testing.assert_array_equal(layout.output_merge_cropped(rcv[r], H), shards[r][c])

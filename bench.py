@@ -23,6 +23,8 @@ rank's local Q shard against the resident global K/V (standing in for the K/V
 all-gather), and the output reverse runs on a resident head-sharded buffer of the
 Ulysses layout.
 
+`joint_segments` (masked workloads) times cp_attn_joint with image and text
+K/V as separate segments, both layouts, against the concatenated call.
 `chunked_kv` times the same share with its K/V arriving in W chunks
 (cp_attn_partial per chunk, then cp_attn_merge).
 
@@ -478,6 +480,28 @@ def chunked_kv(path, burst=10):
     return res
 
 
+def joint_segments(path, burst=10):
+    """The joint workload's attention with image and text K/V as two segments (the text
+    keys re-attached behind or in front of the image keys, text padding mask on the
+    text segment only), against the concatenated masked call."""
+    import torch
+    cp, wl = path.cp, path.wl
+    S_img = wl.S - wl.text_tokens
+    k, v, m = path.attn_k, path.attn_v, path.mask
+    ki, vi = k[:, :S_img].contiguous(), v[:, :S_img].contiguous()
+    kj, vj, jm = k[:, S_img:].contiguous(), v[:, S_img:].contiguous(), m[:, S_img:].contiguous()
+    out = torch.empty_like(path.attn_q)
+    res = {}
+    for name, front in (("rear", False), ("front", True)):
+        def call(front=front):
+            cp.cp_attn_joint(path.attn_q, ki, vi, kj, vj, None, jm, joint_front=front, scale=path.scale, out=out)
+        call()
+        torch.cuda.synchronize()
+        res[f"{name}_us"] = time_burst(call, burst) * 1e3
+    res["concatenated_us"] = time_burst(path.attn, burst) * 1e3
+    return res
+
+
 def uaa_compare(seqs, heads=14, D=128, seed=1240):
     """Per-rank comparison of a padded Ulysses layout against the composed one, at the
     shapes of the pages' attention benchmark (heads 14, D 128, four ranks):
@@ -780,6 +804,11 @@ def main():
         c["note"] = ("local-Q/global-KV share with K/V in W chunks: W partial attentions "
                      "(fp32 O + lse) and one merge, against the dense call")
         out["chunked_kv"] = c
+    if args.only is None and wl.masked:
+        j = joint_segments(path)
+        j["note"] = ("joint attention over image and text K/V segments (text mask only), "
+                     "rear and front layouts, against the concatenated masked call")
+        out["joint_segments"] = j
     if args.only is None:
         out["parity"] = parity_sample(path, wl)
         if not args.no_cpu_baseline:

@@ -36,6 +36,9 @@ SIGNATURES = {
                                                     _i64, ctypes.c_int, _vp]),
     "cp_output_merge_cropped": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                                ctypes.c_int, _vp]),
+    "cp_attn_joint": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i64, _i64,
+                                     _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, _vp,
+                                     ctypes.c_size_t, _vp]),
     "cp_attn_partial": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                        ctypes.c_float, ctypes.c_int, _vp]),
     "cp_attn_merge": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]),
@@ -59,7 +62,7 @@ CP_ERR_WORKSPACE = 11
 
 CP_DTYPE_BF16 = 0
 CP_DTYPE_FP16 = 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _lib = None
 

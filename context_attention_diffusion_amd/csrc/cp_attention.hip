@@ -113,6 +113,21 @@ struct View {
   FastDiv L;       // rows per chunk
 };
 
+// Kernel variants (compile-time): chunked row views, and a second key segment.
+constexpr int kModeChunked = 1;
+constexpr int kModeTwoSeg = 2;
+
+template <bool CHUNKED>
+__device__ __forceinline__ long long row_off_t(const View& v, int i) {
+  if constexpr (!CHUNKED) {
+    return (long long)i * v.rs;
+  } else {
+    uint32_t c, r;
+    v.L.divmod(uint32_t(i), c, r);
+    return (long long)c * v.cs + (long long)r * v.rs;
+  }
+}
+
 __device__ __forceinline__ long long row_off(const View& v, int i) {
   if (!v.chunked) return (long long)i * v.rs;
   uint32_t c, r;
@@ -122,6 +137,15 @@ __device__ __forceinline__ long long row_off(const View& v, int i) {
 
 struct AttnArgs {
   View qv, kv, ov;  // Q, K and V (one view for both), O
+  // Keys come in up to two segments, attended as one sequence in this order:
+  // segment 0 = k, v, mask (Skv keys, tiles [0, nt0)), segment 1 = k1, v1, mask1
+  // (Skv1 keys, dense [B][Skv1][H][D] with K/V's row and head strides, tiles
+  // from nt0 on).  Each segment's last tile may be partial.
+  const __bf16* k1;
+  const __bf16* v1;
+  const uint8_t* mask1;
+  int Skv1;         // 0: one segment
+  int nt0;          // ceil(Skv / BN)
   const __bf16* q;
   const __bf16* k;
   const __bf16* v;
@@ -147,8 +171,10 @@ struct AttnArgs {
 // The body is a device function behind a thin kernel: the LDS address-space
 // casts it needs are device-only, and keeping them out of the kernel itself lets
 // the host pass emit the kernel's launch stub.
-template <int D>
+template <int D, int MODE>
 __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
+  constexpr bool kChunked = (MODE & kModeChunked) != 0;
+  constexpr bool kTwoSeg = (MODE & kModeTwoSeg) != 0;
   using C = Cfg<D>;
   // K and V tiles: one array per (operand, key group, buffer).  Separate objects
   // let the compiler see that a fill of one buffer does not alias the reads of
@@ -178,13 +204,34 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   const __bf16* kbase = a.k + b * a.kv.bs + h * a.kv.hs;
   const __bf16* vbase = a.v + b * a.kv.bs + h * a.kv.hs;
   const uint8_t* mbase = a.mask ? a.mask + size_t(b) * a.Skv : nullptr;
+  const __bf16* kbase1 = kbase;  // segment 1 (two-segment variant only)
+  const __bf16* vbase1 = vbase;
+  const uint8_t* mbase1 = nullptr;
+  if constexpr (kTwoSeg) {
+    const size_t seg1_off = (size_t(b) * a.Skv1) * a.kv.rs + size_t(h) * a.kv.hs;
+    kbase1 = a.k1 + seg1_off;
+    vbase1 = a.v1 + seg1_off;
+    mbase1 = a.mask1 ? a.mask1 + size_t(b) * a.Skv1 : nullptr;
+  }
+  // Segment of tile t and its first key there (one segment: tile t, key t * BN).
+  auto seg_of = [&](int t, bool& s1, int& key0, int& len) {
+    if constexpr (kTwoSeg) {
+      s1 = t >= a.nt0;
+      key0 = (s1 ? t - a.nt0 : t) * C::BN;
+      len = s1 ? a.Skv1 : a.Skv;
+    } else {
+      s1 = false;
+      key0 = t * C::BN;
+      len = a.Skv;
+    }
+  };
 
   // ---- Q fragment (B operand of S^T = K Q^T): query row q_row, d = ks*16 + 8*hi .. +8
   const int q_row = mt * C::BM + gw * 32 + l32;
   bf16x8 qf[C::KS];
   {
     const bool ok = q_row < a.Sq;
-    const __bf16* qp = a.q + b * a.qv.bs + row_off(a.qv, ok ? q_row : 0) + h * a.qv.hs;
+    const __bf16* qp = a.q + b * a.qv.bs + row_off_t<kChunked>(a.qv, ok ? q_row : 0) + h * a.qv.hs;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       bf16x8 t = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + 8 * hi);
@@ -193,7 +240,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     }
   }
 
-  const int n_tiles = (a.Skv + C::BN - 1) / C::BN;
+  const int n_tiles = kTwoSeg ? a.nt0 + (a.Skv1 + C::BN - 1) / C::BN : (a.Skv + C::BN - 1) / C::BN;
   const int n_iter = i1 - i0;  // iterations of every wave in this segment
   // tiles of key group g in the segment: global tiles 2 (i0 + j) + g < n_tiles
   auto tiles_of_group = [&](int g) { return min(n_iter, max(0, (n_tiles - g + 1) / 2 - i0)); };
@@ -215,12 +262,17 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // dst: the destination tile array.
   // The 64 rows of a tile are contiguous at stride rs (a chunked view has chunks
   // of a multiple of 64 rows); rows past the last key are outside the range.
-  auto fill = [&](const __bf16* base, int t, char* dst) {
-    const int key0 = t * C::BN;
-    const int rows = min(C::BN, a.Skv - key0);
+  // which: 0 = K, 1 = V.
+  auto fill = [&](int which, int t, char* dst) {
+    bool s1;
+    int key0, len;
+    seg_of(t, s1, key0, len);
+    const int rows = min(C::BN, len - key0);
+    const __bf16* src = s1 ? (which ? vbase1 : kbase1) + (long long)key0 * a.kv.rs
+                           : (which ? vbase : kbase) + row_off_t<kChunked>(a.kv, key0);
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16*>(base + row_off(a.kv, key0)), (short)0,
-        int(uint32_t(rows - 1) * rs_bytes + uint32_t(D) * 2u), 0x00020000);
+        const_cast<__bf16*>(src), (short)0, int(uint32_t(rows - 1) * rs_bytes + uint32_t(D) * 2u),
+        0x00020000);
 #pragma unroll
     for (int j = 0; j < C::SPT; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -247,9 +299,13 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   uint32_t mraw = 1;
   auto bias_of = [&](int t) {
     if (gt < C::BN) {
-      const int key = t * C::BN + gt;
-      kvalid = key < a.Skv;
-      mraw = mbase ? uint32_t(mbase[kvalid ? key : 0]) : 1u;
+      bool s1;
+      int key0, len;
+      seg_of(t, s1, key0, len);
+      const int key = key0 + gt;
+      kvalid = key < len;
+      const uint8_t* mb = s1 ? mbase1 : mbase;
+      mraw = mb ? uint32_t(mb[kvalid ? key : 0]) : 1u;
     }
   };
   auto store_bias = [&](int buf) {
@@ -288,7 +344,10 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // Bias (tail / mask) and the scaled tile max over this query's 64 keys.
   // Accumulator row r of block kb is key kb*32 + 8*(r/4) + 4*hi + r%4.
   auto bias_max = [&](int buf, int t, f32x16* s) -> float {
-    if (a.mask != nullptr || (t + 1) * C::BN > a.Skv) {
+    bool s1;
+    int key0, len;
+    seg_of(t, s1, key0, len);
+    if ((s1 ? mbase1 : mbase) != nullptr || key0 + C::BN > len) {
       const float* br = bias_row + buf * C::BN;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -377,14 +436,14 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // the one on the critical path.
   if (grp == 0) {
     if (n_g > 0) {
-      fill(kbase, 2 * (i0 + 0) + 0, ktile(I0{}, I0{}));
-      fill(vbase, 2 * (i0 + 0) + 0, vtile(I0{}, I0{}));
+      fill(0, 2 * (i0 + 0) + 0, ktile(I0{}, I0{}));
+      fill(1, 2 * (i0 + 0) + 0, vtile(I0{}, I0{}));
     }
     if (n_g1 > 0) {
-      fill(kbase, 2 * (i0 + 0) + 1, ktile(I1{}, I0{}));
-      fill(vbase, 2 * (i0 + 0) + 1, vtile(I1{}, I0{}));
+      fill(0, 2 * (i0 + 0) + 1, ktile(I1{}, I0{}));
+      fill(1, 2 * (i0 + 0) + 1, vtile(I1{}, I0{}));
     }
-    if (n_g1 > 1) fill(kbase, 2 * (i0 + 1) + 1, ktile(I1{}, I1{}));
+    if (n_g1 > 1) fill(0, 2 * (i0 + 1) + 1, ktile(I1{}, I1{}));
   }
   if (n_g > 0) {
     bias_of(tile_of(0));
@@ -410,13 +469,13 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       if (i < n_g) {
         const bool nx = i + 1 < n_g;
         if (nx) {
-          fill(kbase, 2 * (i0 + i + 1), ktile(I0{}, BQ{}));
-          fill(vbase, 2 * (i0 + i + 1), vtile(I0{}, BQ{}));
+          fill(0, 2 * (i0 + i + 1), ktile(I0{}, BQ{}));
+          fill(1, 2 * (i0 + i + 1), vtile(I0{}, BQ{}));
           bias_of(tile_of(i + 1));
         }
         // group 1's next K (two tiles ahead) and V (one tile ahead)
-        if (i + 2 < n_g1) fill(kbase, 2 * (i0 + i + 2) + 1, ktile(I1{}, BP{}));
-        if (i + 1 < n_g1) fill(vbase, 2 * (i0 + i + 1) + 1, vtile(I1{}, BQ{}));
+        if (i + 2 < n_g1) fill(0, 2 * (i0 + i + 2) + 1, ktile(I1{}, BP{}));
+        if (i + 1 < n_g1) fill(1, 2 * (i0 + i + 1) + 1, vtile(I1{}, BQ{}));
         __builtin_amdgcn_sched_barrier(0);
         qk(ktile(I0{}, BP{}), sc);
         rescale(bias_max(P, tile_of(i), sc));
@@ -527,7 +586,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       return;
     }
     if (q_row < a.Sq) {
-      __bf16* op = a.o + b * a.ov.bs + row_off(a.ov, q_row) + h * a.ov.hs;
+      __bf16* op = a.o + b * a.ov.bs + row_off_t<kChunked>(a.ov, q_row) + h * a.ov.hs;
       // Accumulator row r of block db is d = db*32 + 8*(r/4) + 4*hi + r%4.
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -651,9 +710,9 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
   *reinterpret_cast<bf16x4*>(a.o + r * a.D + c4) = w;
 }
 
-template <int D>
+template <int D, int MODE>
 __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(AttnArgs a) {
-  attn_fwd_body<D>(a);
+  attn_fwd_body<D, MODE>(a);
 }
 
 }  // namespace
@@ -693,7 +752,9 @@ View chunked_view(int64_t B, int64_t L, int64_t H, int64_t hs, int64_t rs) {
 int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* v, const View& kv,
                 const uint8_t* key_mask, __bf16* o, const View& ov, int64_t B, int64_t Sq, int64_t Skv,
                 int64_t H, int64_t D, float scale, void* ws, size_t ws_bytes, size_t ext_q, size_t ext_kv,
-                size_t ext_o, cp_stream_t stream, float* o_part = nullptr, float* lse = nullptr) {
+                size_t ext_o, cp_stream_t stream, float* o_part = nullptr, float* lse = nullptr,
+                const __bf16* k1 = nullptr, const __bf16* v1 = nullptr, const uint8_t* mask1 = nullptr,
+                int64_t Skv1 = 0) {
   const int64_t bm = 32 * kGroupWaves;
   const int64_t m_tiles = (Sq + bm - 1) / bm;
   const int64_t n_work = B * H * m_tiles;
@@ -713,7 +774,12 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
   args.m_tiles = int(m_tiles);
   args.n_work = int(n_work);
   args.sc = scale * 1.4426950408889634f;
-  const int64_t n_tiles = (Skv + 63) / 64;
+  args.k1 = k1;
+  args.v1 = v1;
+  args.mask1 = mask1;
+  args.Skv1 = int(Skv1);
+  args.nt0 = int((Skv + 63) / 64);
+  const int64_t n_tiles = args.nt0 + (Skv1 + 63) / 64;
   args.n_iter_blk = int((n_tiles + 1) / 2);
   args.nsplit = 1;
   args.ws = nullptr;
@@ -729,8 +795,11 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
     if (2 * n_work <= cus && nsplit >= 2) {
       const size_t need = size_t(n_work * nsplit) * size_t(bm) * size_t(D + 2) * sizeof(float);
       if (ws_bytes < need) return CP_ERR_WORKSPACE;
+      const size_t ext1 = size_t(B * Skv1 * H * D) * 2;
       if (overlaps(ws, need, q, ext_q) || overlaps(ws, need, k, ext_kv) || overlaps(ws, need, v, ext_kv) ||
-          overlaps(ws, need, o, ext_o) || (key_mask && overlaps(ws, need, key_mask, size_t(B * Skv))))
+          overlaps(ws, need, o, ext_o) || (key_mask && overlaps(ws, need, key_mask, size_t(B * Skv))) ||
+          (k1 && overlaps(ws, need, k1, ext1)) || (v1 && overlaps(ws, need, v1, ext1)) ||
+          (mask1 && overlaps(ws, need, mask1, size_t(B * Skv1))))
         return CP_ERR_ALIAS;
       args.nsplit = int(nsplit);
       args.ws = static_cast<float*>(ws);
@@ -740,11 +809,18 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
   // combine: BM * D / 4 threads of 256 per query block
   const dim3 grid{unsigned(n_work * args.nsplit)}, block{unsigned(kThreads)}, cblock{256u},
       cgrid{unsigned(n_work * (D / 8))};
+  const int mode = (kv.chunked || qv.chunked || ov.chunked ? kModeChunked : 0) | (Skv1 > 0 ? kModeTwoSeg : 0);
+  if (mode == kModeChunked + kModeTwoSeg) return CP_ERR_UNSUPPORTED;  // no entry point combines them
+  auto launch_fwd = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, args); };
   if (D == 128) {
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, block, 0, s, args);
+    if (mode == 0) launch_fwd(attn_fwd_kernel<128, 0>);
+    else if (mode == kModeChunked) launch_fwd(attn_fwd_kernel<128, kModeChunked>);
+    else launch_fwd(attn_fwd_kernel<128, kModeTwoSeg>);
     if (args.nsplit > 1) hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, cblock, 0, s, args);
   } else {
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, block, 0, s, args);
+    if (mode == 0) launch_fwd(attn_fwd_kernel<64, 0>);
+    else if (mode == kModeChunked) launch_fwd(attn_fwd_kernel<64, kModeChunked>);
+    else launch_fwd(attn_fwd_kernel<64, kModeTwoSeg>);
     if (args.nsplit > 1) hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, cblock, 0, s, args);
   }
   return hip_status(hipGetLastError());
@@ -800,6 +876,51 @@ extern "C" int cp_attn_localq_globalkv_ws(const void* q, const void* k, const vo
                                           int64_t Skv, int64_t H, int64_t D, float scale, int causal,
                                           void* workspace, size_t workspace_bytes, cp_stream_t stream) {
   return attn_run(q, k, v, key_mask, o, B, Sq, Skv, H, D, scale, causal, workspace, workspace_bytes, stream);
+}
+
+extern "C" int cp_attn_joint(const void* q, const void* k_img, const void* v_img, const uint8_t* img_mask,
+                             const void* k_joint, const void* v_joint, const uint8_t* joint_mask, int joint_front,
+                             void* o, int64_t B, int64_t Sq, int64_t S_img, int64_t T, int64_t H, int64_t D,
+                             float scale, int causal, void* workspace, size_t workspace_bytes, cp_stream_t stream) {
+  if (!q || !k_img || !v_img || !o) return CP_ERR_NULL;
+  if (T > 0 && (!k_joint || !v_joint)) return CP_ERR_NULL;
+  if (T < 0 || S_img < 1) return CP_ERR_SHAPE;
+  if (joint_front != 0 && joint_front != 1) return CP_ERR_UNSUPPORTED;
+  constexpr int64_t kIntMax = 0x7fffffff;
+  if (S_img > kIntMax / 2 || T > kIntMax / 2) return CP_ERR_SHAPE;
+  if (const int st = attn_check(B, Sq, S_img + T, H, D, scale, causal)) return st;
+  if (!aligned16(q) || !aligned16(k_img) || !aligned16(v_img) || !aligned16(o)) return CP_ERR_ALIGNMENT;
+  if (T > 0 && (!aligned16(k_joint) || !aligned16(v_joint))) return CP_ERR_ALIGNMENT;
+  if (workspace && !aligned16(workspace)) return CP_ERR_ALIGNMENT;
+  if (B > kIntMax || Sq > kIntMax || S_img + T > kIntMax - 64 || H > kIntMax) return CP_ERR_SHAPE;
+  if (H * D * 2 * 64 > kIntMax) return CP_ERR_SHAPE;
+  const int64_t bm = 32 * kGroupWaves;
+  int64_t bh, n_work, qe, ie, je;
+  if (!mul_capped(B, H, kIntMax, &bh) || !mul_capped(bh, (Sq + bm - 1) / bm, kIntMax, &n_work)) return CP_ERR_SHAPE;
+  if (!mul_capped(B * Sq, H * D, int64_t(1) << 60, &qe) || !mul_capped(B * S_img, H * D, int64_t(1) << 60, &ie) ||
+      !mul_capped(B * (T > 0 ? T : 1), H * D, int64_t(1) << 60, &je))
+    return CP_ERR_SHAPE;
+  const size_t qb = size_t(qe) * 2, ib = size_t(ie) * 2, jb = size_t(je) * 2;
+  if (overlaps(o, qb, q, qb) || overlaps(o, qb, k_img, ib) || overlaps(o, qb, v_img, ib)) return CP_ERR_ALIAS;
+  if (T > 0 && (overlaps(o, qb, k_joint, jb) || overlaps(o, qb, v_joint, jb))) return CP_ERR_ALIAS;
+  if (img_mask && overlaps(o, qb, img_mask, size_t(B * S_img))) return CP_ERR_ALIAS;
+  if (T > 0 && joint_mask && overlaps(o, qb, joint_mask, size_t(B * T))) return CP_ERR_ALIAS;
+  const auto* qp = static_cast<const __bf16*>(q);
+  const auto* ki = static_cast<const __bf16*>(k_img);
+  const auto* vi = static_cast<const __bf16*>(v_img);
+  const auto* kj = static_cast<const __bf16*>(k_joint);
+  const auto* vj = static_cast<const __bf16*>(v_joint);
+  auto* op = static_cast<__bf16*>(o);
+  if (T == 0)
+    return attn_launch(qp, plain_view(Sq, H, D), ki, vi, plain_view(S_img, H, D), img_mask, op, plain_view(Sq, H, D),
+                       B, Sq, S_img, H, D, scale, workspace, workspace_bytes, qb, ib, qb, stream);
+  if (joint_front)
+    return attn_launch(qp, plain_view(Sq, H, D), kj, vj, plain_view(T, H, D), joint_mask, op, plain_view(Sq, H, D),
+                       B, Sq, T, H, D, scale, workspace, workspace_bytes, qb, jb, qb, stream, nullptr, nullptr,
+                       ki, vi, img_mask, S_img);
+  return attn_launch(qp, plain_view(Sq, H, D), ki, vi, plain_view(S_img, H, D), img_mask, op, plain_view(Sq, H, D),
+                     B, Sq, S_img, H, D, scale, workspace, workspace_bytes, qb, ib, qb, stream, nullptr, nullptr,
+                     kj, vj, joint_mask, T);
 }
 
 extern "C" int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, void* send, int64_t B,

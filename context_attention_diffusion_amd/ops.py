@@ -210,6 +210,53 @@ def cp_attn_localq_globalkv(q, k, v, key_mask=None, scale=None, out=None, causal
     return out
 
 
+def cp_attn_joint(q, k_img, v_img, k_joint=None, v_joint=None, img_mask=None, joint_mask=None,
+                  joint_front=False, scale=None, out=None, causal=False, stream=None, split=True,
+                  workspace=None) -> torch.Tensor:
+    """Attention of q [B,Sq,H,D] over two key segments, image [B,S_img,H,D] and joint
+    [B,T,H,D] (None: T = 0), in the order joint_front selects, with per-segment uint8
+    masks (None = all valid)."""
+    lib = _lib.load()
+    B, Sq, H, D = q.shape
+    S_img = k_img.shape[1]
+    if k_img.shape != (B, S_img, H, D) or v_img.shape != k_img.shape:
+        raise ValueError("k_img, v_img must be [B, S_img, H, D] matching q")
+    T = 0 if k_joint is None else k_joint.shape[1]
+    if T and (k_joint.shape != (B, T, H, D) or v_joint is None or v_joint.shape != k_joint.shape):
+        raise ValueError("k_joint, v_joint must be [B, T, H, D] matching q")
+    for t in (q, k_img, v_img) + ((k_joint, v_joint) if T else ()):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("attention takes bfloat16")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+
+    def mask_ptr(m, n, name):
+        if m is None:
+            return None
+        if m.dtype not in (torch.uint8, torch.bool) or tuple(m.shape) != (B, n):
+            raise ValueError(f"{name} must be uint8/bool [B, {n}]")
+        return _dev(m, name)
+
+    im = mask_ptr(img_mask, S_img, "img_mask")
+    jm = mask_ptr(joint_mask, T, "joint_mask") if T else None
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    ws_ptr, ws_bytes = None, 0
+    if split:
+        need = int(lib.cp_attn_workspace_bytes(B, Sq, S_img + T, H, D))
+        if workspace is None:
+            workspace = staging_buffer("attn_workspace", (max(need, 16),), torch.uint8, q.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel()
+    _lib.check("cp_attn_joint", lib.cp_attn_joint(
+        _dev(q, "q"), _dev(k_img, "k_img"), _dev(v_img, "v_img"), im,
+        _dev(k_joint, "k_joint") if T else None, _dev(v_joint, "v_joint") if T else None, jm,
+        int(bool(joint_front)), _dev(out, "o"), B, Sq, S_img, T, H, D, float(scale), int(bool(causal)),
+        ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
 def cp_attn_partial(q, k, v, key_mask=None, scale=None, out=None, lse=None, causal=False,
                     stream=None):
     """Attention over one K/V chunk: (o_part fp32 [B,Sq,H,D], lse fp32 [B,H,Sq], natural log).

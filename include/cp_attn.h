@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CP_ABI_VERSION 5
+#define CP_ABI_VERSION 6
 
 typedef struct ihipStream_t* cp_stream_t; /* == hipStream_t */
 
@@ -220,6 +220,35 @@ int cp_attn_localq_globalkv_ws(const void* q, const void* k, const void* v,
  * per compute unit).  0 for an unsupported D.  No GPU work, no allocation.
  */
 size_t cp_attn_workspace_bytes(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D);
+
+/*
+ * Joint text/image attention of the composed Ulysses x AllGather-KV layout
+ * ([vllm-omni#7641]: the Ulysses step keeps the head-sliced joint (text) K/V
+ * aside, the AllGather-KV step gathers the image K/V and re-attaches the joint
+ * tensors in front of or behind them; the review-fix commits merge the 2D key
+ * masks against that final key layout, filling a missing side with "attend").
+ * The keys are the two segments in that order, each with its own optional
+ * mask, attended as one sequence without building the concatenation:
+ *
+ *   keys = joint_front ? [joint | image] : [image | joint]
+ *   mask = the same concatenation of img_mask and joint_mask (NULL = all valid)
+ *   o[b,i,h,:] = sum_{j valid} softmax_j(scale * q[b,i,h,:] . key_j) value_j
+ *
+ *   q, o              : [B][Sq][H][D] bf16
+ *   k_img, v_img      : [B][S_img][H][D] bf16;  img_mask   : NULL or [B][S_img] uint8
+ *   k_joint, v_joint  : [B][T][H][D] bf16;      joint_mask : NULL or [B][T] uint8
+ *   joint_front       : 1 = joint keys first, 0 = image keys first
+ *   workspace         : as for cp_attn_localq_globalkv_ws (sized for Skv = S_img + T), or NULL
+ *
+ * T == 0 (no joint tokens; k_joint/v_joint may be NULL) is plain attention over
+ * the image keys.  Requires S_img >= 1, T >= 0, the attention's conditions, and
+ * o disjoint from every input.  The result equals cp_attn_localq_globalkv on
+ * the concatenated keys, values and mask up to the order of summation.
+ */
+int cp_attn_joint(const void* q, const void* k_img, const void* v_img, const uint8_t* img_mask,
+                  const void* k_joint, const void* v_joint, const uint8_t* joint_mask, int joint_front,
+                  void* o, int64_t B, int64_t Sq, int64_t S_img, int64_t T, int64_t H, int64_t D,
+                  float scale, int causal, void* workspace, size_t workspace_bytes, cp_stream_t stream);
 
 /*
  * Attention over keys that arrive in chunks: a forward pass over one K/V chunk

@@ -182,3 +182,28 @@ def merge_partials(o_parts, lses):
                 w = np.exp(lk - m)
                 out[b, i, h, :] = (w[:, None] * o_parts[:, b, i, h, :]).sum(axis=0) / w.sum()
     return out
+
+
+# ------------------------------------------------ joint text/image key segments
+#
+# The composed Ulysses x AllGather-KV path of [vllm-omni#7641] re-attaches the
+# head-sliced joint (text) K/V to the gathered image K/V, in front or behind,
+# and merges the 2D key masks against that final layout: a missing side is
+# filled with "attend" and the result is a [B, K_final] mask.  Attention then
+# runs over the concatenation.
+
+
+def joint_attention(q, k_img, v_img, k_joint, v_joint, img_mask=None, joint_mask=None,
+                    joint_front=False, scale=None):
+    """Attention over keys ``[joint | image]`` (front) or ``[image | joint]`` (rear)."""
+    B, S_img = k_img.shape[:2]
+    T = 0 if k_joint is None else k_joint.shape[1]
+    im = np.ones((B, S_img), dtype=np.uint8) if img_mask is None else np.asarray(img_mask, dtype=np.uint8)
+    if T == 0:
+        return attention(q, k_img, v_img, im, scale)
+    jm = np.ones((B, T), dtype=np.uint8) if joint_mask is None else np.asarray(joint_mask, dtype=np.uint8)
+    if joint_front:
+        k, v, m = (np.concatenate(x, axis=1) for x in ((k_joint, k_img), (v_joint, v_img), (jm, im)))
+    else:
+        k, v, m = (np.concatenate(x, axis=1) for x in ((k_img, k_joint), (v_img, v_joint), (im, jm)))
+    return attention(q, k, v, m, scale)

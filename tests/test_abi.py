@@ -134,6 +134,15 @@ def _merge(**kw):
     return _lib.load().cp_attn_merge(a["p"], a["l"], a["N"], a["o"], a["B"], a["Sq"], a["H"], a["D"], None)
 
 
+def _joint(**kw):
+    a = dict(q=A, ki=A + BIG, vi=A + 2 * BIG, im=None, kj=A + 3 * BIG, vj=A + 4 * BIG, jm=None, front=0,
+             o=A + 5 * BIG, B=1, Sq=8, Si=64, T=16, H=2, D=128, scale=0.125, causal=0, ws=None, nbytes=0)
+    a.update(kw)
+    return _lib.load().cp_attn_joint(a["q"], a["ki"], a["vi"], a["im"], a["kj"], a["vj"], a["jm"], a["front"],
+                                     a["o"], a["B"], a["Sq"], a["Si"], a["T"], a["H"], a["D"], a["scale"],
+                                     a["causal"], a["ws"], a["nbytes"], None)
+
+
 def _rev(**kw):
     a = dict(phase=0, s=A, d=A + BIG, B=1, Sl=4, Hl=2, D=128, W=2, dtype=BF16)
     a.update(kw)
@@ -303,6 +312,24 @@ def test_pack_padded_rejects(kw, code):
 ])
 def test_merge_cropped_rejects(kw, code):
     assert _merge_crop(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.CP_ERR_NULL),
+    (dict(kj=None), _lib.CP_ERR_NULL),               # joint tokens without joint keys
+    (dict(T=-1), _lib.CP_ERR_SHAPE),
+    (dict(Si=0), _lib.CP_ERR_SHAPE),
+    (dict(front=2), _lib.CP_ERR_UNSUPPORTED),
+    (dict(D=96), _lib.CP_ERR_HEAD_DIM),
+    (dict(causal=1), _lib.CP_ERR_UNSUPPORTED),
+    (dict(vj=A + 4 * BIG + 8), _lib.CP_ERR_ALIGNMENT),
+    (dict(o=A + 3 * BIG + 32), _lib.CP_ERR_ALIAS),  # o overlaps k_joint
+    (dict(jm=A + 5 * BIG + 8), _lib.CP_ERR_ALIAS),  # joint mask inside o
+    (dict(ws=A + 6 * BIG, nbytes=16, Si=4096), _lib.CP_ERR_WORKSPACE),
+])
+def test_joint_rejects(kw, code):
+    assert _joint(**kw) == code
 
 
 def test_workspace_bytes():

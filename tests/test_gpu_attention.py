@@ -357,3 +357,70 @@ def test_chunked_kv_arrival_full_size_sampled(gu):
     rows = [(0, int(rng.integers(wl.attn_rows)), int(rng.integers(wl.H))) for _ in range(32)]
     ref = OA.attention_rows(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), rows)
     _assert_close(np.stack([got[b, i, h] for b, i, h in rows]), ref, "chunked image_cp4 sampled")
+
+
+# ------------------------------------------------- joint text/image key segments
+
+@pytest.mark.parametrize("B,H,Sq,S_img,T,D,front,im_on,jm_on", [
+    (1, 2, 130, 256, 77, 128, True, False, True),     # ragged joint segment first
+    (2, 3, 70, 130, 64, 64, False, True, True),       # ragged image segment first
+    (1, 1, 33, 64, 1, 128, True, True, False),        # one joint key
+    (2, 2, 129, 500, 200, 128, False, False, False),  # no masks
+    (1, 2, 64, 300, 0, 64, False, True, False),       # no joint tokens
+])
+def test_joint_segments_match_oracle(gu, B, H, Sq, S_img, T, D, front, im_on, jm_on):
+    import context_attention_diffusion_amd as cp
+    seed = 6000 + Sq + S_img + T + D
+    q = _rand_bits((B, Sq, H, D), seed)
+    ki, vi = _rand_bits((B, S_img, H, D), seed + 1), _rand_bits((B, S_img, H, D), seed + 2)
+    kj = _rand_bits((B, T, H, D), seed + 3) if T else None
+    vj = _rand_bits((B, T, H, D), seed + 4) if T else None
+    rng = np.random.default_rng(seed + 5)
+    im = (rng.random((B, S_img)) > 0.3).astype(np.uint8) if im_on else None
+    jm = None
+    if jm_on and T:
+        jm = np.ones((B, T), dtype=np.uint8)
+        for b in range(B):
+            jm[b, int(rng.integers(1, T + 1)):] = 0     # text padding after L_b tokens
+    if im is not None:
+        im[:, 0] = 1
+    dev = lambda x: None if x is None else (torch.from_numpy(x).to(gu.DEV) if x.dtype == np.uint8 else gu.to_dev(x))
+    print(f"[attn] joint B={B} H={H} Sq={Sq} S_img={S_img} T={T} D={D} front={front} masks={im_on},{jm_on}",
+          flush=True)
+    got = cp.cp_attn_joint(dev(q), dev(ki), dev(vi), dev(kj), dev(vj), dev(im), dev(jm), joint_front=front)
+    torch.cuda.synchronize()
+    f = bf16.bits_to_f64
+    ref = OA.joint_attention(f(q), f(ki), f(vi), None if kj is None else f(kj), None if vj is None else f(vj),
+                             im, jm, joint_front=front)
+    _assert_close(gu.to_f64(got), ref, f"joint S_img{S_img} T{T} front{int(front)}")
+
+
+def test_joint_cfg_workload_segments(gu):
+    """The joint CFG workload as two segments (4096 image keys, 512 text keys with the
+    per-batch text padding mask): rear layout equals the concatenated masked call bit
+    for bit (same tiles), front layout within the tolerance, sampled rows vs oracle."""
+    import context_attention_diffusion_amd as cp
+    wl = workloads.WORKLOADS["joint_cfg_cp4"]
+    q, k, v = workloads.global_qkv(wl)
+    q = np.ascontiguousarray(q[:, :wl.attn_rows])
+    S_img = wl.S - wl.text_tokens
+    mask = workloads.key_mask(wl)
+    ki, vi = np.ascontiguousarray(k[:, :S_img]), np.ascontiguousarray(v[:, :S_img])
+    kj, vj = np.ascontiguousarray(k[:, S_img:]), np.ascontiguousarray(v[:, S_img:])
+    jm = np.ascontiguousarray(mask[:, S_img:])
+    assert mask[:, :S_img].all()
+    print("[attn] joint workload segments", flush=True)
+    qd = gu.to_dev(q)
+    rear = cp.cp_attn_joint(qd, gu.to_dev(ki), gu.to_dev(vi), gu.to_dev(kj), gu.to_dev(vj), None,
+                            torch.from_numpy(jm).to(gu.DEV))
+    front = cp.cp_attn_joint(qd, gu.to_dev(ki), gu.to_dev(vi), gu.to_dev(kj), gu.to_dev(vj), None,
+                             torch.from_numpy(jm).to(gu.DEV), joint_front=True)
+    dense = cp.cp_attn_localq_globalkv(qd, gu.to_dev(k), gu.to_dev(v), torch.from_numpy(mask).to(gu.DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(rear, dense), "rear joint layout differs from the concatenated call"
+    assert np.abs(gu.to_f64(front) - gu.to_f64(dense)).max() <= 2e-2
+    rng = np.random.default_rng(wl.seed + 21)
+    rows = [(int(rng.integers(wl.B)), int(rng.integers(wl.attn_rows)), int(rng.integers(wl.H))) for _ in range(32)]
+    ref = OA.attention_rows(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), rows, mask)
+    g = gu.to_f64(front)
+    _assert_close(np.stack([g[b, i, h] for b, i, h in rows]), ref, "joint front sampled")

@@ -292,6 +292,37 @@ def test_uaa_padded_ranks_reassemble_full_attention(W, H):
     assert sum(x[0].shape[2] for x in ins) == H_pad
 
 
+@pytest.mark.parametrize("front", [False, True])
+def test_joint_segments_equal_attention_over_valid_keys_only(front):
+    # masked keys contribute nothing: joint attention equals plain attention over the
+    # valid image keys and valid text keys gathered by hand; front and rear agree
+    B, Sq, S_img, T, H, D = 2, 5, 11, 6, 2, 4
+    q = _rand((B, Sq, H, D), 70)
+    ki, vi = _rand((B, S_img, H, D), 71), _rand((B, S_img, H, D), 72)
+    kj, vj = _rand((B, T, H, D), 73), _rand((B, T, H, D), 74)
+    im = _mask(B, S_img, 75)
+    jm = np.ones((B, T), dtype=np.uint8)
+    jm[0, 2:] = 0          # batch 0: two valid text tokens
+    got = A.joint_attention(q, ki, vi, kj, vj, im, jm, joint_front=front)
+    for b in range(B):
+        kk = np.concatenate([ki[b][im[b] != 0], kj[b][jm[b] != 0]])[None]
+        vv = np.concatenate([vi[b][im[b] != 0], vj[b][jm[b] != 0]])[None]
+        np.testing.assert_allclose(got[b:b + 1], A.attention(q[b:b + 1], kk, vv), rtol=1e-12, atol=1e-13)
+    other = A.joint_attention(q, ki, vi, kj, vj, im, jm, joint_front=not front)
+    np.testing.assert_allclose(got, other, rtol=1e-12, atol=1e-13)
+
+
+def test_joint_without_text_or_masks():
+    B, Sq, S_img, T, H, D = 1, 3, 7, 4, 1, 4
+    q, ki, vi = _rand((B, Sq, H, D), 76), _rand((B, S_img, H, D), 77), _rand((B, S_img, H, D), 78)
+    np.testing.assert_allclose(A.joint_attention(q, ki, vi, None, None), A.attention(q, ki, vi),
+                               rtol=1e-14)
+    # all text masked out: only the image keys count
+    kj, vj = _rand((B, T, H, D), 79), _rand((B, T, H, D), 80)
+    np.testing.assert_allclose(A.joint_attention(q, ki, vi, kj, vj, None, np.zeros((B, T), np.uint8)),
+                               A.attention(q, ki, vi), rtol=1e-12, atol=1e-13)
+
+
 def test_bf16_widening_is_exact():
     bits = np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0x4049, 0x7F80, 0x0001, 0x7F7F],
                     dtype=np.uint16)

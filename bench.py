@@ -77,6 +77,9 @@ def parse():
     p.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench and of "
                         "--calib-copy into a traffic summary; no GPU work")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the fused-chain, chunked-K/V and joint-segment sections (so a kernel "
+                        "trace of the run holds only the headline step's launches)")
     p.add_argument("--uaa", action="store_true",
                    help="per-rank comparison of head padding (usp4+uaa) and the composed U2xA2 "
                         "layout at heads 14, D 128; prints its own JSON line")
@@ -791,7 +794,7 @@ def main():
                               "pack_frac_hbm_peak": pc / PEAK_HBM_GBPS,
                               "unpack_frac_hbm_peak": uc / PEAK_HBM_GBPS,
                               "note": "rotating buffer sets, over 600 MB of reads per pass (misses the 256 MB MALL)"}
-    if args.only is None and not path.two_d:
+    if args.only is None and not path.two_d and not args.no_extras:
         u = ulysses_chain(path)
         u["fused_attn_TFLOPs"] = flops / (u["fused_attn_us"] * 1e-6) / 1e12
         u["fused_step_TFLOPs"] = flops / (u["fused_step_us"] * 1e-6) / 1e12
@@ -804,7 +807,7 @@ def main():
         c["note"] = ("local-Q/global-KV share with K/V in W chunks: W partial attentions "
                      "(fp32 O + lse) and one merge, against the dense call")
         out["chunked_kv"] = c
-    if args.only is None and wl.masked:
+    if args.only is None and wl.masked and not args.no_extras:
         j = joint_segments(path)
         j["note"] = ("joint attention over image and text K/V segments (text mask only), "
                      "rear and front layouts, against the concatenated masked call")

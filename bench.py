@@ -234,7 +234,8 @@ def run_steps(path, n, events=None, only=None):
 def cold_layout_gbps(wl, dev, rounds=4):
     """Pack and unpack with rotating buffer sets whose READ footprint alone exceeds 600 MB,
     so each launch's loads miss the 256 MB Infinity Cache whatever the stores leave resident
-    there (nontemporal stores do not evict the read sets).  Returns (pack GB/s, unpack GB/s)."""
+    there (nontemporal stores do not evict the read sets).  Returns (pack GB/s, unpack GB/s,
+    GB/s of torch's device copy of the same bytes, as three tensor copies, for reference)."""
     import torch
 
     import context_attention_diffusion_amd as cp
@@ -249,14 +250,17 @@ def cold_layout_gbps(wl, dev, rounds=4):
         outs = tuple(torch.empty((B, W * Sl, H // W, D), dtype=torch.bfloat16, device=dev)
                      for _ in range(3))
         sets.append((x, st, outs))
+    copy_dst = {id(st): torch.empty_like(st) for _, st, _ in sets}
     res = []
-    for which in ("pack", "unpack"):
+    for which in ("pack", "unpack", "copy"):
         def launch(sset):
             x, st, outs = sset
             if which == "pack":
                 cp.cp_pack_qkv_dst_major(*x, W, staging=st)
-            else:
+            elif which == "unpack":
                 cp.cp_unpack_head_sharded(st, B, W, out=outs)
+            else:   # reference: one device copy of the same bytes (staging -> a buffer of its size)
+                copy_dst[id(st)].copy_(st)
         for sset in sets:
             launch(sset)
         torch.cuda.synchronize()
@@ -264,7 +268,7 @@ def cold_layout_gbps(wl, dev, rounds=4):
         it = iter(order * 2)
         ms = time_burst(lambda: launch(next(it)), len(order))
         res.append(wl.pack_bytes() / (ms * 1e-3) / 1e9)
-    del sets
+    del sets, copy_dst
     torch.cuda.empty_cache()
     return res
 
@@ -789,10 +793,11 @@ def main():
                            "algorithmic_flops_per_launch": flops}
     out["kernels"] = kern
     if args.only is None and not args.no_cold:
-        pc, uc = cold_layout_gbps(wl, dev)
+        pc, uc, cc = cold_layout_gbps(wl, dev)
         out["layout_cold"] = {"pack_GBps": pc, "unpack_GBps": uc,
                               "pack_frac_hbm_peak": pc / PEAK_HBM_GBPS,
                               "unpack_frac_hbm_peak": uc / PEAK_HBM_GBPS,
+                              "torch_copy_same_bytes_GBps": cc,
                               "note": "rotating buffer sets, over 600 MB of reads per pass (misses the 256 MB MALL)"}
     if args.only is None and not path.two_d and not args.no_extras:
         u = ulysses_chain(path)

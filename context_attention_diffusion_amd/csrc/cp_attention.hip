@@ -328,18 +328,20 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   };
   const int vaddr0 = vaddr_of(0), vaddr1 = vaddr_of(1);
 
-  // S^T[key][query] of one tile (two 32-key blocks).
+  // S^T[key][query] of one tile (two 32-key blocks).  The two blocks' MFMA chains
+  // are interleaved step by step, so each chain's dependent MFMA and each K read
+  // have the other chain's MFMA to hide behind.
   auto qk = [&](const char* kt, f32x16* s) {
+    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < C::KS; ++kk) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * C::RB + (kaddr ^ (kk * 32)));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc, 0, 0, 0);
-      }
-      s[kb] = acc;
+    for (int kk = 0; kk < C::KS; ++kk) {
+      const bf16x8 kf0 = *reinterpret_cast<const bf16x8*>(kt + (kaddr ^ (kk * 32)));
+      const bf16x8 kf1 = *reinterpret_cast<const bf16x8*>(kt + 32 * C::RB + (kaddr ^ (kk * 32)));
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[kk], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[kk], acc1, 0, 0, 0);
     }
+    s[0] = acc0;
+    s[1] = acc1;
   };
   // Bias (tail / mask) and the scaled tile max over this query's 64 keys.
   // Accumulator row r of block kb is key kb*32 + 8*(r/4) + 4*hi + r%4.

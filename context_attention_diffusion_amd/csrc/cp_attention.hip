@@ -117,19 +117,11 @@ struct View {
 constexpr int kModeChunked = 1;
 constexpr int kModeTwoSeg = 2;
 
+// CHUNKED = false: every view of the kernel is plain.  CHUNKED = true: a view may
+// be chunked (each view says whether it is).
 template <bool CHUNKED>
 __device__ __forceinline__ long long row_off_t(const View& v, int i) {
-  if constexpr (!CHUNKED) {
-    return (long long)i * v.rs;
-  } else {
-    uint32_t c, r;
-    v.L.divmod(uint32_t(i), c, r);
-    return (long long)c * v.cs + (long long)r * v.rs;
-  }
-}
-
-__device__ __forceinline__ long long row_off(const View& v, int i) {
-  if (!v.chunked) return (long long)i * v.rs;
+  if (!CHUNKED || !v.chunked) return (long long)i * v.rs;
   uint32_t c, r;
   v.L.divmod(uint32_t(i), c, r);
   return (long long)c * v.cs + (long long)r * v.rs;
@@ -661,7 +653,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   w[1] = (__bf16)(acc.y * inv);
   w[2] = (__bf16)(acc.z * inv);
   w[3] = (__bf16)(acc.w * inv);
-  *reinterpret_cast<bf16x4*>(a.o + b * a.ov.bs + row_off(a.ov, q_row) + h * a.ov.hs + c4) = w;
+  *reinterpret_cast<bf16x4*>(a.o + b * a.ov.bs + row_off_t<true>(a.ov, q_row) + h * a.ov.hs + c4) = w;
 }
 
 // Merge of N partial attentions of the same queries over disjoint key sets:

@@ -514,20 +514,30 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   }
 
   // ---- merge the two groups' softmax states through LDS (reusing the K tile
-  // arrays: O of group-1 wave gw in one array each, m and l in the first V array)
-  float* comb = reinterpret_cast<float*>(gw == 0 ? k00 : gw == 1 ? k01 : gw == 2 ? k10 : k11);
+  // arrays: O of group-1 wave gw in one array each, as float4 columns that
+  // consecutive lanes read at consecutive 16-byte slots; m and l in the first V
+  // array).  Group 0 issues all its reads before using any.
+  float4* comb4 = reinterpret_cast<float4*>(gw == 0 ? k00 : gw == 1 ? k01 : gw == 2 ? k10 : k11);
   float* comb_ml = reinterpret_cast<float*>(v00) + gw * 2 * 64;
   auto slot = [&](int k) { return k * 64 + lane; };
+  auto cslot = [&](int db, int g) { return (db * 4 + g) * 64 + lane; };
   if (grp == 1) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) comb[slot(db * 16 + r)] = acc_o[db][r];
+      for (int g = 0; g < 4; ++g)
+        comb4[cslot(db, g)] =
+            make_float4(acc_o[db][4 * g], acc_o[db][4 * g + 1], acc_o[db][4 * g + 2], acc_o[db][4 * g + 3]);
     comb_ml[slot(0)] = m_run;
     comb_ml[slot(1)] = l_run;
   }
   __syncthreads();
   if (grp == 0) {
+    float4 cb[C::DB][4];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) cb[db][g] = comb4[cslot(db, g)];
     const float m1 = comb_ml[slot(0)];
     const float l1 = comb_ml[slot(1)];
     const float mm = fmaxf(m_run, m1);
@@ -543,10 +553,10 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           float4 w;
-          w.x = acc_o[db][4 * g + 0] * a0 + comb[slot(db * 16 + 4 * g + 0)] * a1;
-          w.y = acc_o[db][4 * g + 1] * a0 + comb[slot(db * 16 + 4 * g + 1)] * a1;
-          w.z = acc_o[db][4 * g + 2] * a0 + comb[slot(db * 16 + 4 * g + 2)] * a1;
-          w.w = acc_o[db][4 * g + 3] * a0 + comb[slot(db * 16 + 4 * g + 3)] * a1;
+          w.x = acc_o[db][4 * g + 0] * a0 + cb[db][g].x * a1;
+          w.y = acc_o[db][4 * g + 1] * a0 + cb[db][g].y * a1;
+          w.z = acc_o[db][4 * g + 2] * a0 + cb[db][g].z * a1;
+          w.w = acc_o[db][4 * g + 3] * a0 + cb[db][g].w * a1;
           *reinterpret_cast<float4*>(wp + db * 32 + 8 * g + 4 * hi) = w;
         }
       if (hi == 0) {
@@ -566,10 +576,10 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             float4 w;
-            w.x = acc_o[db][4 * g + 0] * c0 + comb[slot(db * 16 + 4 * g + 0)] * c1;
-            w.y = acc_o[db][4 * g + 1] * c0 + comb[slot(db * 16 + 4 * g + 1)] * c1;
-            w.z = acc_o[db][4 * g + 2] * c0 + comb[slot(db * 16 + 4 * g + 2)] * c1;
-            w.w = acc_o[db][4 * g + 3] * c0 + comb[slot(db * 16 + 4 * g + 3)] * c1;
+            w.x = acc_o[db][4 * g + 0] * c0 + cb[db][g].x * c1;
+            w.y = acc_o[db][4 * g + 1] * c0 + cb[db][g].y * c1;
+            w.z = acc_o[db][4 * g + 2] * c0 + cb[db][g].z * c1;
+            w.w = acc_o[db][4 * g + 3] * c0 + cb[db][g].w * c1;
             *reinterpret_cast<float4*>(pp + db * 32 + 8 * g + 4 * hi) = w;
           }
         // sum_j e^{z_j} = 2^mm * l_tot, with mm and l_tot in the kernel's log2 units
@@ -590,7 +600,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            w[e] = (__bf16)(acc_o[db][r] * c0 + comb[slot(db * 16 + r)] * c1);
+            w[e] = (__bf16)(acc_o[db][r] * c0 + cb[db][g][e] * c1);
           }
           *reinterpret_cast<bf16x4*>(op + db * 32 + 8 * g + 4 * hi) = w;
         }

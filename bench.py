@@ -453,7 +453,10 @@ def ulysses_chain(path, burst=10):
 
 def chunked_kv(path, burst=10):
     """The local-Q/global-KV share with K/V arriving in W chunks (one per AllGather
-    rank): W cp_attn_partial calls and one cp_attn_merge, against the dense call."""
+    rank): W cp_attn_partial calls and one cp_attn_merge; or cp_attn_partial on the
+    first chunk and cp_attn_partial_accum on the others (the last one writing the
+    output); against the dense call.  last_chunk_accumulate_us is what remains after
+    the last chunk arrives."""
     import torch
     cp, wl = path.cp, path.wl
     W, Sl = wl.W, wl.S_local
@@ -473,8 +476,23 @@ def chunked_kv(path, burst=10):
     def merge():
         cp.cp_attn_merge(o_parts, lses, out=out)
 
+    st_o = torch.empty((B, Sq, H, D), dtype=torch.float32, device=q.device)
+    st_l = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    out_acc = torch.empty_like(q)
+
+    def accumulate():
+        cp.cp_attn_partial(q, ks[0], vs[0], ms[0], scale=path.scale, out=st_o, lse=st_l)
+        for r in range(1, W):
+            cp.cp_attn_partial_accum(q, ks[r], vs[r], st_o, st_l, ms[r], scale=path.scale,
+                                     final=r == W - 1, out=out_acc)
+
+    def last_accumulate():
+        cp.cp_attn_partial_accum(q, ks[W - 1], vs[W - 1], st_o, st_l, ms[W - 1], scale=path.scale,
+                                 final=True, out=out_acc)
+
     partials()
     merge()
+    accumulate()
     torch.cuda.synchronize()
     dense = path.o_attn
     path.attn()
@@ -482,7 +500,10 @@ def chunked_kv(path, burst=10):
     res = {"chunks": W, "partials_us": time_burst(partials, burst) * 1e3,
            "merge_us": time_burst(merge, burst) * 1e3,
            "merge_bytes": int(o_parts.numel() * 4 + lses.numel() * 4 + out.numel() * 2),
-           "max_abs_diff_vs_dense": float((out.float() - dense.float()).abs().max())}
+           "max_abs_diff_vs_dense": float((out.float() - dense.float()).abs().max()),
+           "accumulate_us": time_burst(accumulate, burst) * 1e3,
+           "last_chunk_accumulate_us": time_burst(last_accumulate, burst) * 1e3,
+           "accumulate_max_abs_diff_vs_dense": float((out_acc.float() - dense.float()).abs().max())}
     res["merge_GBps"] = res["merge_bytes"] / (res["merge_us"] * 1e-6) / 1e9
     return res
 

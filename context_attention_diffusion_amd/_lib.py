@@ -41,6 +41,8 @@ SIGNATURES = {
                                      ctypes.c_size_t, _vp]),
     "cp_attn_partial": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                        ctypes.c_float, ctypes.c_int, _vp]),
+    "cp_attn_partial_accum": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                             _i64, ctypes.c_float, ctypes.c_int, _vp]),
     "cp_attn_merge": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]),
     "cp_attn_recv_to_send": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                             ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t, _vp]),
@@ -62,7 +64,7 @@ CP_ERR_WORKSPACE = 11
 
 CP_DTYPE_BF16 = 0
 CP_DTYPE_FP16 = 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _lib = None
 

@@ -158,6 +158,10 @@ struct AttnArgs {
   // lse = ln(sum of exp(scale q.k) over the valid keys) [B][H][Sq] fp32.
   float* o_part;
   float* lse;
+  // Running state of an attention over earlier key chunks (same format as
+  // o_part / lse), folded into this call's result; NULL: none.
+  const float* st_o;
+  const float* st_lse;
 };
 
 // The body is a device function behind a thin kernel: the LDS address-space
@@ -568,24 +572,73 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     }
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const float c0 = a0 * inv, c1 = a1 * inv;
-    if (a.o_part != nullptr) {
+    if (a.o_part != nullptr || a.st_o != nullptr) {
+      // This call's normalised output and lse over its keys, folded into the running
+      // state when there is one: L = ln(e^lse_s + e^lse_k), O = e^(lse_s - L) O_s +
+      // e^(lse_k - L) O_k.  Output: fp32 O and L (o_part, lse), or bf16 O (o).
       if (q_row < a.Sq) {
-        float* pp = a.o_part + ((size_t(b) * a.Sq + q_row) * a.H + h) * D;
+        const size_t orow = ((size_t(b) * a.Sq + q_row) * a.H + h) * D;
+        const size_t lidx = (size_t(b) * a.H + h) * a.Sq + q_row;
+        // sum_j e^{z_j} = 2^mm * l_tot, with mm and l_tot in the kernel's log2 units
+        const float lse_k = l_tot > 0.f ? (mm + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+        float L = lse_k, wk = 1.f, ws = 0.f;
+        const float* sp = nullptr;
+        if (a.st_o != nullptr) {
+          const float lse_s = a.st_lse[lidx];
+          if (lse_s != -INFINITY) {
+            sp = a.st_o + orow;
+            if (lse_k == -INFINITY) {
+              L = lse_s;
+              ws = 1.f;
+              wk = 0.f;
+            } else {
+              L = fmaxf(lse_s, lse_k) + log1pf(expf(-fabsf(lse_s - lse_k)));
+              ws = expf(lse_s - L);
+              wk = expf(lse_k - L);
+            }
+          }
+        }
+        const float k0 = c0 * wk, k1 = c1 * wk;
+        float4 out[C::DB][4];
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             float4 w;
-            w.x = acc_o[db][4 * g + 0] * c0 + cb[db][g].x * c1;
-            w.y = acc_o[db][4 * g + 1] * c0 + cb[db][g].y * c1;
-            w.z = acc_o[db][4 * g + 2] * c0 + cb[db][g].z * c1;
-            w.w = acc_o[db][4 * g + 3] * c0 + cb[db][g].w * c1;
-            *reinterpret_cast<float4*>(pp + db * 32 + 8 * g + 4 * hi) = w;
+            w.x = acc_o[db][4 * g + 0] * k0 + cb[db][g].x * k1;
+            w.y = acc_o[db][4 * g + 1] * k0 + cb[db][g].y * k1;
+            w.z = acc_o[db][4 * g + 2] * k0 + cb[db][g].z * k1;
+            w.w = acc_o[db][4 * g + 3] * k0 + cb[db][g].w * k1;
+            if (sp != nullptr) {
+              const float4 sv = *reinterpret_cast<const float4*>(sp + db * 32 + 8 * g + 4 * hi);
+              w.x += ws * sv.x;
+              w.y += ws * sv.y;
+              w.z += ws * sv.z;
+              w.w += ws * sv.w;
+            }
+            out[db][g] = w;
           }
-        // sum_j e^{z_j} = 2^mm * l_tot, with mm and l_tot in the kernel's log2 units
-        if (hi == 0)
-          a.lse[(size_t(b) * a.H + h) * a.Sq + q_row] =
-              l_tot > 0.f ? (mm + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+        if (a.o_part != nullptr) {
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *reinterpret_cast<float4*>(a.o_part + orow + db * 32 + 8 * g + 4 * hi) = out[db][g];
+          if (hi == 0) a.lse[lidx] = L;
+        } else {
+          __bf16* op = a.o + b * a.ov.bs + row_off_t<kChunked>(a.ov, q_row) + h * a.ov.hs;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              bf16x4 w;
+              w[0] = (__bf16)out[db][g].x;
+              w[1] = (__bf16)out[db][g].y;
+              w[2] = (__bf16)out[db][g].z;
+              w[3] = (__bf16)out[db][g].w;
+              *reinterpret_cast<bf16x4*>(op + db * 32 + 8 * g + 4 * hi) = w;
+            }
+        }
       }
       return;
     }
@@ -757,6 +810,7 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
                 const uint8_t* key_mask, __bf16* o, const View& ov, int64_t B, int64_t Sq, int64_t Skv,
                 int64_t H, int64_t D, float scale, void* ws, size_t ws_bytes, size_t ext_q, size_t ext_kv,
                 size_t ext_o, cp_stream_t stream, float* o_part = nullptr, float* lse = nullptr,
+                const float* st_o = nullptr, const float* st_lse = nullptr,
                 const __bf16* k1 = nullptr, const __bf16* v1 = nullptr, const uint8_t* mask1 = nullptr,
                 int64_t Skv1 = 0) {
   const int64_t bm = 32 * kGroupWaves;
@@ -789,6 +843,8 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
   args.ws = nullptr;
   args.o_part = o_part;
   args.lse = lse;
+  args.st_o = st_o;
+  args.st_lse = st_lse;
   // Split the key range of every query block into nsplit parts when the query
   // blocks alone would occupy at most half of the compute units; each part
   // keeps at least kMinSplitIters iterations.
@@ -920,11 +976,11 @@ extern "C" int cp_attn_joint(const void* q, const void* k_img, const void* v_img
                        B, Sq, S_img, H, D, scale, workspace, workspace_bytes, qb, ib, qb, stream);
   if (joint_front)
     return attn_launch(qp, plain_view(Sq, H, D), kj, vj, plain_view(T, H, D), joint_mask, op, plain_view(Sq, H, D),
-                       B, Sq, T, H, D, scale, workspace, workspace_bytes, qb, jb, qb, stream, nullptr, nullptr,
-                       ki, vi, img_mask, S_img);
+                       B, Sq, T, H, D, scale, workspace, workspace_bytes, qb, jb, qb, stream, nullptr, nullptr, nullptr,
+                       nullptr, ki, vi, img_mask, S_img);
   return attn_launch(qp, plain_view(Sq, H, D), ki, vi, plain_view(S_img, H, D), img_mask, op, plain_view(Sq, H, D),
-                     B, Sq, S_img, H, D, scale, workspace, workspace_bytes, qb, ib, qb, stream, nullptr, nullptr,
-                     kj, vj, joint_mask, T);
+                     B, Sq, S_img, H, D, scale, workspace, workspace_bytes, qb, ib, qb, stream, nullptr, nullptr, nullptr,
+                     nullptr, kj, vj, joint_mask, T);
 }
 
 extern "C" int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, void* send, int64_t B,
@@ -959,13 +1015,19 @@ extern "C" int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, v
                      D, scale, workspace, workspace_bytes, rb, rb, sb, stream);
 }
 
-extern "C" int cp_attn_partial(const void* q, const void* k, const void* v, const uint8_t* key_mask,
-                               void* o_part, void* lse, int64_t B, int64_t Sq, int64_t Skv, int64_t H,
-                               int64_t D, float scale, int causal, cp_stream_t stream) {
-  if (!q || !k || !v || !o_part || !lse) return CP_ERR_NULL;
+namespace {
+
+// Checks and launch shared by cp_attn_partial and cp_attn_partial_accum.
+// out_o / out_lse: fp32 outputs (may be the state itself); o_final: bf16 output.
+int partial_run(const void* q, const void* k, const void* v, const uint8_t* key_mask, void* out_o,
+                void* out_lse, const void* st_o, const void* st_lse, void* o_final, int64_t B, int64_t Sq,
+                int64_t Skv, int64_t H, int64_t D, float scale, int causal, cp_stream_t stream) {
   if (const int st = attn_check(B, Sq, Skv, H, D, scale, causal)) return st;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part)) return CP_ERR_ALIGNMENT;
-  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return CP_ERR_ALIGNMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return CP_ERR_ALIGNMENT;
+  if ((out_o && !aligned16(out_o)) || (st_o && !aligned16(st_o)) || (o_final && !aligned16(o_final)))
+    return CP_ERR_ALIGNMENT;
+  if ((reinterpret_cast<uintptr_t>(out_lse) & 3u) != 0 || (reinterpret_cast<uintptr_t>(st_lse) & 3u) != 0)
+    return CP_ERR_ALIGNMENT;
   constexpr int64_t kIntMax = 0x7fffffff;
   if (B > kIntMax || Sq > kIntMax || Skv > kIntMax - 64 || H > kIntMax) return CP_ERR_SHAPE;
   if (H * D * 2 * 64 > kIntMax) return CP_ERR_SHAPE;
@@ -977,17 +1039,46 @@ extern "C" int cp_attn_partial(const void* q, const void* k, const void* v, cons
     return CP_ERR_SHAPE;
   const size_t qb = size_t(qe) * 2, kb = size_t(ke) * 2, pb = size_t(qe) * 4, lb = size_t(B * H * Sq) * 4;
   const size_t mb = key_mask ? size_t(B * Skv) : 0;
-  for (const auto& out : {std::make_pair(static_cast<const void*>(o_part), pb),
-                          std::make_pair(static_cast<const void*>(lse), lb)}) {
-    if (overlaps(out.first, out.second, q, qb) || overlaps(out.first, out.second, k, kb) ||
-        overlaps(out.first, out.second, v, kb) || (key_mask && overlaps(out.first, out.second, key_mask, mb)))
+  // every buffer this call writes or keeps must be disjoint from the inputs it reads
+  struct Range { const void* p; size_t n; };
+  const Range writes[] = {{out_o, pb}, {out_lse, lb}, {o_final, qb}, {st_o, pb}, {st_lse, lb}};
+  for (const Range& w : writes) {
+    if (!w.p) continue;
+    if (overlaps(w.p, w.n, q, qb) || overlaps(w.p, w.n, k, kb) || overlaps(w.p, w.n, v, kb) ||
+        (key_mask && overlaps(w.p, w.n, key_mask, mb)))
       return CP_ERR_ALIAS;
   }
-  if (overlaps(o_part, pb, lse, lb)) return CP_ERR_ALIAS;
+  if (out_o && out_lse && overlaps(out_o, pb, out_lse, lb)) return CP_ERR_ALIAS;
+  if (st_o && st_lse && overlaps(st_o, pb, st_lse, lb)) return CP_ERR_ALIAS;
+  if (o_final && ((st_o && overlaps(o_final, qb, st_o, pb)) || (st_lse && overlaps(o_final, qb, st_lse, lb))))
+    return CP_ERR_ALIAS;
   return attn_launch(static_cast<const __bf16*>(q), plain_view(Sq, H, D), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), plain_view(Skv, H, D), key_mask, nullptr,
-                     plain_view(Sq, H, D), B, Sq, Skv, H, D, scale, nullptr, 0, qb, kb, pb, stream,
-                     static_cast<float*>(o_part), static_cast<float*>(lse));
+                     static_cast<const __bf16*>(v), plain_view(Skv, H, D), key_mask,
+                     static_cast<__bf16*>(o_final), plain_view(Sq, H, D), B, Sq, Skv, H, D, scale, nullptr, 0,
+                     qb, kb, o_final ? qb : pb, stream, static_cast<float*>(out_o), static_cast<float*>(out_lse),
+                     static_cast<const float*>(st_o), static_cast<const float*>(st_lse));
+}
+
+}  // namespace
+
+extern "C" int cp_attn_partial(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                               void* o_part, void* lse, int64_t B, int64_t Sq, int64_t Skv, int64_t H,
+                               int64_t D, float scale, int causal, cp_stream_t stream) {
+  if (!q || !k || !v || !o_part || !lse) return CP_ERR_NULL;
+  return partial_run(q, k, v, key_mask, o_part, lse, nullptr, nullptr, nullptr, B, Sq, Skv, H, D, scale, causal,
+                     stream);
+}
+
+extern "C" int cp_attn_partial_accum(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                                     void* state_o, void* state_lse, void* o_final, int64_t B, int64_t Sq,
+                                     int64_t Skv, int64_t H, int64_t D, float scale, int causal,
+                                     cp_stream_t stream) {
+  if (!q || !k || !v || !state_o || !state_lse) return CP_ERR_NULL;
+  if (o_final)
+    return partial_run(q, k, v, key_mask, nullptr, nullptr, state_o, state_lse, o_final, B, Sq, Skv, H, D, scale,
+                       causal, stream);
+  return partial_run(q, k, v, key_mask, state_o, state_lse, state_o, state_lse, nullptr, B, Sq, Skv, H, D, scale,
+                     causal, stream);
 }
 
 extern "C" int cp_attn_merge(const void* o_parts, const void* lses, int64_t N, void* o, int64_t B, int64_t Sq,

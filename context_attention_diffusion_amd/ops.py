@@ -290,6 +290,43 @@ def cp_attn_partial(q, k, v, key_mask=None, scale=None, out=None, lse=None, caus
     return out, lse
 
 
+def cp_attn_partial_accum(q, k, v, state_o, state_lse, key_mask=None, scale=None, final=False, out=None,
+                          causal=False, stream=None):
+    """Fold attention over one more K/V chunk into a running state (fp32 state_o [B,Sq,H,D],
+    state_lse [B,H,Sq], as cp_attn_partial writes them).  final=False updates the state in
+    place and returns (state_o, state_lse); final=True returns the merged bf16 output."""
+    lib = _lib.load()
+    B, Sq, H, D = q.shape
+    Skv = k.shape[1]
+    if k.shape != (B, Skv, H, D) or v.shape != k.shape:
+        raise ValueError("k, v must be [B, Skv, H, D] matching q")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("attention takes bfloat16 q, k, v")
+    if tuple(state_o.shape) != (B, Sq, H, D) or state_o.dtype != torch.float32:
+        raise ValueError("state_o must be float32 [B, Sq, H, D]")
+    if tuple(state_lse.shape) != (B, H, Sq) or state_lse.dtype != torch.float32:
+        raise ValueError("state_lse must be float32 [B, H, Sq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    mask_ptr = None
+    if key_mask is not None:
+        if key_mask.dtype not in (torch.uint8, torch.bool) or tuple(key_mask.shape) != (B, Skv):
+            raise ValueError("key_mask must be uint8/bool [B, Skv]")
+        mask_ptr = _dev(key_mask, "key_mask")
+    o_ptr = None
+    if final:
+        if out is None:
+            out = torch.empty_like(q)
+        if out.shape != q.shape or out.dtype != torch.bfloat16:
+            raise ValueError("out must match q")
+        o_ptr = _dev(out, "o_final")
+    _lib.check("cp_attn_partial_accum", lib.cp_attn_partial_accum(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), mask_ptr, _dev(state_o, "state_o"),
+        _dev(state_lse, "state_lse"), o_ptr, B, Sq, Skv, H, D, float(scale), int(bool(causal)),
+        _stream(stream)))
+    return out if final else (state_o, state_lse)
+
+
 def cp_attn_merge(o_parts, lses, out=None, stream=None) -> torch.Tensor:
     """Merge partial results: o_parts fp32 [N,B,Sq,H,D], lses fp32 [N,B,H,Sq] -> bf16 [B,Sq,H,D]."""
     lib = _lib.load()

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CP_ABI_VERSION 6
+#define CP_ABI_VERSION 7
 
 typedef struct ihipStream_t* cp_stream_t; /* == hipStream_t */
 
@@ -272,6 +272,30 @@ int cp_attn_joint(const void* q, const void* k_img, const void* v_img, const uin
 int cp_attn_partial(const void* q, const void* k, const void* v, const uint8_t* key_mask,
                     void* o_part, void* lse, int64_t B, int64_t Sq, int64_t Skv, int64_t H,
                     int64_t D, float scale, int causal, cp_stream_t stream);
+
+/*
+ * Attention over the next key chunk folded into a running state, for K/V that
+ * arrive chunk by chunk (same definitions as cp_attn_partial and cp_attn_merge;
+ * the merge happens in this call's epilogue, so no partial buffers and no merge
+ * launch are needed).  The state is a partial result in cp_attn_partial's
+ * format: state_o [B][Sq][H][D] fp32 (normalised) and state_lse [B][H][Sq]
+ * fp32; a row whose state_lse is -inf has no contribution yet (its state_o is
+ * not read).  With L = ln(e^state_lse + e^lse_chunk):
+ *
+ *   merged = e^(state_lse - L) state_o + e^(lse_chunk - L) o_chunk
+ *
+ *   o_final == NULL : the state is updated in place (state_o = merged, state_lse = L)
+ *   o_final != NULL : merged is written to o_final [B][Sq][H][D] as bf16 (RNE) and
+ *                     the state is left unchanged (the last chunk)
+ *
+ * A sequence: cp_attn_partial on the first chunk (or a state with lse = -inf),
+ * then cp_attn_partial_accum on each further chunk, o_final given on the last.
+ * The state must not overlap q, k, v or key_mask; o_final must not overlap
+ * anything.  Other conditions as for cp_attn_partial.
+ */
+int cp_attn_partial_accum(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                          void* state_o, void* state_lse, void* o_final, int64_t B, int64_t Sq, int64_t Skv,
+                          int64_t H, int64_t D, float scale, int causal, cp_stream_t stream);
 
 /*
  * Merge of N partial results of the same queries over disjoint key sets:

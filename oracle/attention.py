@@ -164,6 +164,26 @@ def attention_partial(q, k, v, key_mask=None, scale=None, chunk=256):
     return out, lse
 
 
+def accumulate_partial(state_o, state_lse, o_k, lse_k):
+    """Running state after one more key chunk: the merge of two partial results, as
+    ``(o, lse)`` with ``lse = ln(e^state_lse + e^lse_k)`` (rows with both -inf stay
+    -inf with zero output)."""
+    state_o, o_k = np.asarray(state_o, np.float64), np.asarray(o_k, np.float64)
+    state_lse, lse_k = np.asarray(state_lse, np.float64), np.asarray(lse_k, np.float64)
+    lse = np.logaddexp(state_lse, lse_k)
+    B, Sq, H, D = o_k.shape
+    out = np.zeros_like(o_k)
+    for b in range(B):
+        for h in range(H):
+            for i in range(Sq):
+                if lse[b, h, i] == -np.inf:
+                    continue
+                ws = 0.0 if state_lse[b, h, i] == -np.inf else np.exp(state_lse[b, h, i] - lse[b, h, i])
+                wk = 0.0 if lse_k[b, h, i] == -np.inf else np.exp(lse_k[b, h, i] - lse[b, h, i])
+                out[b, i, h] = ws * state_o[b, i, h] + wk * o_k[b, i, h]
+    return out, lse
+
+
 def merge_partials(o_parts, lses):
     """``o_parts`` ``[N, B, Sq, H, D]`` and ``lses`` ``[N, B, H, Sq]`` -> merged ``[B, Sq, H, D]``."""
     o_parts = np.asarray(o_parts, dtype=np.float64)

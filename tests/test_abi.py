@@ -128,6 +128,14 @@ def _partial(**kw):
                                        a["Skv"], a["H"], a["D"], a["scale"], a["causal"], None)
 
 
+def _accum(**kw):
+    a = dict(q=A, k=A + BIG, v=A + 2 * BIG, m=None, so=A + 3 * BIG, sl=A + 4 * BIG, of=None, B=1, Sq=8,
+             Skv=16, H=2, D=128, scale=0.125, causal=0)
+    a.update(kw)
+    return _lib.load().cp_attn_partial_accum(a["q"], a["k"], a["v"], a["m"], a["so"], a["sl"], a["of"], a["B"],
+                                             a["Sq"], a["Skv"], a["H"], a["D"], a["scale"], a["causal"], None)
+
+
 def _merge(**kw):
     a = dict(p=A, l=A + BIG, N=2, o=A + 2 * BIG, B=1, Sq=8, H=2, D=128)
     a.update(kw)
@@ -268,6 +276,22 @@ def test_recv_to_send_rejects(kw, code):
 ])
 def test_partial_rejects(kw, code):
     assert _partial(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(so=None), _lib.CP_ERR_NULL),
+    (dict(sl=None), _lib.CP_ERR_NULL),
+    (dict(D=96), _lib.CP_ERR_HEAD_DIM),
+    (dict(so=A + 3 * BIG + 8), _lib.CP_ERR_ALIGNMENT),
+    (dict(of=A + 5 * BIG + 8), _lib.CP_ERR_ALIGNMENT),
+    (dict(so=A + BIG + 64), _lib.CP_ERR_ALIAS),          # state inside k
+    (dict(sl=A + 3 * BIG + 64), _lib.CP_ERR_ALIAS),      # lse inside state_o
+    (dict(of=A + 3 * BIG), _lib.CP_ERR_ALIAS),           # final output over the state
+    (dict(of=A + 32), _lib.CP_ERR_ALIAS),                # final output over q
+])
+def test_partial_accum_rejects(kw, code):
+    assert _accum(**kw) == code
 
 
 @cpu_only

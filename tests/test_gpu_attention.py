@@ -424,3 +424,57 @@ def test_joint_cfg_workload_segments(gu):
     ref = OA.attention_rows(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), rows, mask)
     g = gu.to_f64(front)
     _assert_close(np.stack([g[b, i, h] for b, i, h in rows]), ref, "joint front sampled")
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,D,cuts,masked", [
+    (1, 2, 130, 1133, 128, (100, 433), False),
+    (2, 3, 70, 300, 64, (64, 65), True),
+    (2, 2, 257, 700, 128, (350,), True),
+])
+def test_partial_accumulate_matches_oracle(gu, B, H, Sq, Skv, D, cuts, masked):
+    """partial(chunk 0) -> accumulate in place (middle chunks) -> accumulate with final
+    bf16 output; the first chunk of a masked case has no valid key at all."""
+    import context_attention_diffusion_amd as cp
+    seed = 5000 + Sq + Skv + D
+    q = _rand_bits((B, Sq, H, D), seed)
+    k = _rand_bits((B, Skv, H, D), seed + 1)
+    v = _rand_bits((B, Skv, H, D), seed + 2)
+    mask = None
+    edges = [0, *cuts, Skv]
+    if masked:
+        mask = (np.random.default_rng(seed + 3).random((B, Skv)) > 0.4).astype(np.uint8)
+        mask[:, :edges[1]] = 0
+        mask[:, -1] = 1
+    print(f"[attn] accumulate B={B} H={H} Sq={Sq} Skv={Skv} D={D} cuts={cuts} masked={masked}", flush=True)
+    qd = gu.to_dev(q)
+    f = bf16.bits_to_f64
+    qf, kf, vf = f(q), f(k), f(v)
+
+    def chunk(a, b):
+        kd = gu.to_dev(np.ascontiguousarray(k[:, a:b]))
+        vd = gu.to_dev(np.ascontiguousarray(v[:, a:b]))
+        md = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask[:, a:b])).to(gu.DEV)
+        mk = None if mask is None else mask[:, a:b]
+        return kd, vd, md, mk
+
+    kd, vd, md, mk = chunk(edges[0], edges[1])
+    st_o, st_l = cp.cp_attn_partial(qd, kd, vd, md)
+    ref_o, ref_l = OA.attention_partial(qf, kf[:, :edges[1]], vf[:, :edges[1]], mk)
+    for a, b in zip(edges[1:-2], edges[2:-1]):
+        kd, vd, md, mk = chunk(a, b)
+        cp.cp_attn_partial_accum(qd, kd, vd, st_o, st_l, md)
+        ref_o, ref_l = OA.accumulate_partial(ref_o, ref_l, *OA.attention_partial(qf, kf[:, a:b], vf[:, a:b], mk))
+    torch.cuda.synchronize()
+    got_l = st_l.double().cpu().numpy()
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(np.isfinite(got_l), fin)
+    if fin.any():
+        assert np.abs(got_l[fin] - ref_l[fin]).max() <= LSE_ERR
+        rows = np.repeat(fin.transpose(0, 2, 1)[..., None], D, axis=3)
+        _assert_close(st_o.double().cpu().numpy()[rows], ref_o[rows], "accumulated state")
+    kd, vd, md, _ = chunk(edges[-2], edges[-1])
+    before = st_o.clone()
+    out = cp.cp_attn_partial_accum(qd, kd, vd, st_o, st_l, md, final=True)
+    torch.cuda.synchronize()
+    assert torch.equal(before, st_o), "the final call must leave the state unchanged"
+    _assert_close(gu.to_f64(out), OA.attention(qf, kf, vf, mask), "accumulated final")

@@ -245,6 +245,24 @@ def test_chunked_keys_merge_to_full_attention(masked, cuts):
     np.testing.assert_allclose(lse_all, np.logaddexp.reduce(lses, axis=0), rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("masked", [False, True])
+def test_folding_chunks_one_by_one_is_full_attention(masked):
+    # state = partial(chunk 0); state = accumulate(state, partial(chunk i)) ... equals
+    # attention and log-sum-exp over all keys; a leading fully masked chunk is a no-op
+    B, Sq, Skv, H, D = 2, 6, 40, 2, 4
+    q, k, v = _rand((B, Sq, H, D), 81), _rand((B, Skv, H, D), 82), _rand((B, Skv, H, D), 83)
+    m = _mask(B, Skv, 84) if masked else np.ones((B, Skv), np.uint8)
+    m[:, :5] = 0
+    edges = [0, 5, 17, 18, 40]
+    st_o, st_l = A.attention_partial(q, k[:, :5], v[:, :5], m[:, :5])
+    assert np.all(st_l == -np.inf)
+    for a, b in zip(edges[1:-1], edges[2:]):
+        o_k, l_k = A.attention_partial(q, k[:, a:b], v[:, a:b], m[:, a:b])
+        st_o, st_l = A.accumulate_partial(st_o, st_l, o_k, l_k)
+    np.testing.assert_allclose(st_o, A.attention(q, k, v, m), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(st_l, A.attention_partial(q, k, v, m)[1], rtol=1e-12, atol=1e-12)
+
+
 def test_partial_lse_closed_forms():
     # Q = 0: every z = 0, so lse = ln(number of valid keys); one valid key: lse = its z
     B, Sq, Skv, H, D = 2, 3, 10, 1, 4

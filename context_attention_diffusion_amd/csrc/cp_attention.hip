@@ -175,9 +175,12 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // K and V tiles: one array per (operand, key group, buffer).  Separate objects
   // let the compiler see that a fill of one buffer does not alias the reads of
   // another, so no wait for the in-flight fills is inserted before those reads.
-  __shared__ __attribute__((aligned(1024))) char k00[C::TILE], k01[C::TILE], k10[C::TILE], k11[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char v00[C::TILE], v01[C::TILE], v10[C::TILE], v11[C::TILE];
-  __shared__ __attribute__((aligned(16))) float bias_all[kGroups * 2 * C::BN];
+  // The compiler lays __shared__ arrays out in name order: the V tiles come first,
+  // inside the 64 KB that a ds_read's 16-bit offset reaches, so every transposed V
+  // read takes its tile base as an immediate instead of an address add.
+  __shared__ __attribute__((aligned(1024))) char lds0_v00[C::TILE], lds0_v01[C::TILE], lds0_v10[C::TILE], lds0_v11[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char lds1_k00[C::TILE], lds1_k01[C::TILE], lds1_k10[C::TILE], lds1_k11[C::TILE];
+  __shared__ __attribute__((aligned(16))) float lds2_bias[kGroups * 2 * C::BN];
 
   const int tid = threadIdx.x;
   // Wave-uniform indices go through readfirstlane so that the compiler keeps
@@ -277,16 +280,16 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // Tile arrays of key group G, buffer B (both compile-time).
   auto ktile = [&](auto g, auto bf) -> char* {
     constexpr int G = decltype(g)::value, B = decltype(bf)::value;
-    return G == 0 ? (B == 0 ? k00 : k01) : (B == 0 ? k10 : k11);
+    return G == 0 ? (B == 0 ? lds1_k00 : lds1_k01) : (B == 0 ? lds1_k10 : lds1_k11);
   };
   auto vtile = [&](auto g, auto bf) -> char* {
     constexpr int G = decltype(g)::value, B = decltype(bf)::value;
-    return G == 0 ? (B == 0 ? v00 : v01) : (B == 0 ? v10 : v11);
+    return G == 0 ? (B == 0 ? lds0_v00 : lds0_v01) : (B == 0 ? lds0_v10 : lds0_v11);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   const int n_g1 = tiles_of_group(1);  // tiles of group 1 (local tile i is global tile 2(i0 + i) + 1)
-  float* bias_row = bias_all + grp * 2 * C::BN;
+  float* bias_row = lds2_bias + grp * 2 * C::BN;
 
   // Key validity of tile t as an additive bias, one key per thread of wave 0.
   // The mask byte is loaded here and only compared when the bias row is
@@ -521,8 +524,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // arrays: O of group-1 wave gw in one array each, as float4 columns that
   // consecutive lanes read at consecutive 16-byte slots; m and l in the first V
   // array).  Group 0 issues all its reads before using any.
-  float4* comb4 = reinterpret_cast<float4*>(gw == 0 ? k00 : gw == 1 ? k01 : gw == 2 ? k10 : k11);
-  float* comb_ml = reinterpret_cast<float*>(v00) + gw * 2 * 64;
+  float4* comb4 = reinterpret_cast<float4*>(gw == 0 ? lds1_k00 : gw == 1 ? lds1_k01 : gw == 2 ? lds1_k10 : lds1_k11);
+  float* comb_ml = reinterpret_cast<float*>(lds0_v00) + gw * 2 * 64;
   auto slot = [&](int k) { return k * 64 + lane; };
   auto cslot = [&](int db, int g) { return (db * 4 + g) * 64 + lane; };
   if (grp == 1) {

@@ -315,6 +315,17 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // K operand of S^T: row kb*32 + l32, chunk 2*kk + hi  ->  byte kb*32*RB + (kaddr ^ (kk * 32))
   const int kswz = C::swz(l32);
   const int kaddr = l32 * C::RB + ((hi ^ (kswz & 1)) * 16) + (kswz & ~1) * 16;
+  // With D = 128 the K tiles lie above the 64 KB that a ds_read offset reaches
+  // (the V tiles fill it): the per-step lane addresses are kept kKHigh bytes high,
+  // opaque to the optimiser so it cannot fold the constant back, and reads address
+  // from tile - kKHigh, so the tile base and the 32-key block fit the offset field.
+  constexpr int kKHigh = 4 * C::TILE >= 65536 ? 65536 : 0;
+  uint32_t kx[C::KS];
+#pragma unroll
+  for (int kk = 0; kk < C::KS; ++kk) {
+    kx[kk] = uint32_t(kaddr ^ (kk * 32)) + uint32_t(kKHigh);
+    asm volatile("" : "+v"(kx[kk]));
+  }
   // V^T operand: lane (G = lane/16, i = lane%16) reads row 16m + 8r + 4hi + i/4, head-dim
   // 32db + 16(G%2) + 4(i%4) .. +4  ->  byte (16m + 8r) * RB + (vaddr_r ^ (db * 64))
   // (r = 0 / 1 for the first / second four keys of the step).
@@ -334,8 +345,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < C::KS; ++kk) {
-      const bf16x8 kf0 = *reinterpret_cast<const bf16x8*>(kt + (kaddr ^ (kk * 32)));
-      const bf16x8 kf1 = *reinterpret_cast<const bf16x8*>(kt + 32 * C::RB + (kaddr ^ (kk * 32)));
+      const bf16x8 kf0 = *reinterpret_cast<const bf16x8*>(kt - kKHigh + kx[kk]);
+      const bf16x8 kf1 = *reinterpret_cast<const bf16x8*>(kt - kKHigh + 32 * C::RB + kx[kk]);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[kk], acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[kk], acc1, 0, 0, 0);
     }

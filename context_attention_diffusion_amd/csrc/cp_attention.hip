@@ -96,8 +96,23 @@ struct Cfg {
   }
 };
 
-__device__ __forceinline__ float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
+// Reductions over the lane pair (l, l ^ 32) that holds one query: v_permlane32_swap
+// of x with itself leaves x in one result and the partner lane's x in the other.
+__device__ __forceinline__ void pair_of(float x, float& u, float& w) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  u = __uint_as_float(r[0]);
+  w = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_max(float x) {
+  float u, w;
+  pair_of(x, u, w);
+  return fmaxf(u, w);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float u, w;
+  pair_of(x, u, w);
+  return u + w;
+}
 
 // Row addressing of one operand: element (b, i, h, d) of a [B][S][H][D] view
 // lies at  b * bs + row_off(i) + h * hs + d  elements from the base, with

@@ -448,6 +448,48 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       m_run = m_new;
     }
   };
+  // Half-tile pieces (keys 32*kb .. 32*kb + 31) of the softmax, the P V product
+  // and the Q K^T chain, for interleaving one tile's second half with the next
+  // tile's first.
+  auto softmax_part = [&](const f32x16* s, int kb, bf16x8* pf) -> float {
+    float lsum = 0.f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+    for (int m = 2 * kb; m < 2 * kb + 2; ++m) {
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        pf[m][kk] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][8 * (m & 1) + kk], a.sc, -m_use));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x2 pr = {pf[m][2 * j], pf[m][2 * j + 1]};
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+      }
+    }
+    return lsum;
+  };
+  auto pv_part = [&](const char* vt, const bf16x8* pf, int kb) {
+#pragma unroll
+    for (int m = 2 * kb; m < 2 * kb + 2; ++m)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const i16x4 lo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + 16 * m * C::RB + (vaddr0 ^ (db * 64))));
+        const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vt + (16 * m + 8) * C::RB + (vaddr1 ^ (db * 64))));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[m], acc_o[db], 0, 0, 0);
+      }
+  };
+  auto qk_part = [&](const char* kt, f32x16* s, int kb) {
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt - kKHigh + kb * 32 * C::RB + kx[kk]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc, 0, 0, 0);
+    }
+    s[kb] = acc;
+  };
   auto prob_pv = [&](const char* vt) {
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     bf16x8 pf[4];
@@ -529,12 +571,21 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
         const bool nx = i + 1 < n_g, nk = i + 2 < n_g;
         if (nk) bias_of(tile_of(i + 2));
         __builtin_amdgcn_sched_barrier(0);
-        prob_pv(vtile(I1{}, BP{}));
-        __builtin_amdgcn_sched_barrier(0);
-        if (nx) {
-          qk(ktile(I1{}, BQ{}), sc);
-          rescale(bias_max(1 - P, tile_of(i + 1), sc));
+        // tile i's softmax and P V in two halves, each followed by the matching half
+        // of tile i+1's Q K^T (computed unconditionally: on the last tile it reads an
+        // idle buffer and is discarded)
+        {
+          bf16x8 pf[4];
+          float lsum = softmax_part(sc, 0, pf);
+          pv_part(vtile(I1{}, BP{}), pf, 0);
+          qk_part(ktile(I1{}, BQ{}), sc, 0);
+          lsum += softmax_part(sc, 1, pf);
+          pv_part(vtile(I1{}, BP{}), pf, 1);
+          qk_part(ktile(I1{}, BQ{}), sc, 1);
+          l_run += lsum;
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (nx) rescale(bias_max(1 - P, tile_of(i + 1), sc));
         if (nk) store_bias(P);
       }
       __builtin_amdgcn_s_waitcnt(0x0f70);

@@ -103,10 +103,22 @@ __device__ __forceinline__ void pair_of(float x, float& u, float& w) {
   u = __uint_as_float(r[0]);
   w = __uint_as_float(r[1]);
 }
+// Maximum of scores, which are finite or -inf (never NaN): the instructions
+// themselves, without the canonicalisation fmaxf needs for signalling NaNs.
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ float pair_max(float x) {
   float u, w;
   pair_of(x, u, w);
-  return fmaxf(u, w);
+  return max2(u, w);
 }
 __device__ __forceinline__ float pair_sum(float x) {
   float u, w;
@@ -387,11 +399,12 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
           s[kb][4 * g + 3] += bb.w;
         }
     }
-    float mx = s[0][0];
+    float mx = max3(s[0][0], s[0][1], s[0][2]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+    for (int r = 3; r < 15; r += 2) mx = max3(mx, s[0][r], s[0][r + 1]);
+    mx = max3(mx, s[0][15], s[1][0]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    for (int r = 1; r < 16; r += 2) mx = max3(mx, s[1][r], s[1][r + 1 < 16 ? r + 1 : r]);
     return pair_max(mx) * a.sc;
   };
   // Probabilities in B-operand order (step m uses block m/2, rows 8*(m%2) .. +8)
@@ -431,6 +444,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   };
 
   float m_run = -INFINITY;  // running max, scaled log2 units (shared by lanes l, l^32)
+  float nm_use = 0.f;       // -m_run, or 0 while m_run is -inf (the softmax's offset)
   float l_run = 0.f;        // this lane's partial row sum
   f32x16 sc[2];             // scores of one tile
 
@@ -446,6 +460,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
       m_run = m_new;
+      nm_use = m_run == -INFINITY ? 0.f : -m_run;
     }
   };
   // Half-tile pieces (keys 32*kb .. 32*kb + 31) of the softmax, the P V product
@@ -454,12 +469,11 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   auto softmax_part = [&](const f32x16* s, int kb, bf16x8* pf) -> float {
     float lsum = 0.f;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
     for (int m = 2 * kb; m < 2 * kb + 2; ++m) {
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
-        pf[m][kk] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][8 * (m & 1) + kk], a.sc, -m_use));
+        pf[m][kk] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][8 * (m & 1) + kk], a.sc, nm_use));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bf16x2 pr = {pf[m][2 * j], pf[m][2 * j + 1]};
@@ -491,9 +505,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     s[kb] = acc;
   };
   auto prob_pv = [&](const char* vt) {
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     bf16x8 pf[4];
-    const float lsum = softmax(sc, m_use, pf);
+    const float lsum = softmax(sc, -nm_use, pf);
     pv(vt, pf);
     l_run += lsum;
   };
@@ -562,6 +575,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     if (n_g > 0) {
       qk(ktile(I1{}, I0{}), sc);
       m_run = bias_max(0, tile_of(0), sc);
+      nm_use = m_run == -INFINITY ? 0.f : -m_run;
     }
     auto iter1 = [&](auto par, int i) {
       constexpr int P = decltype(par)::value;

@@ -226,6 +226,8 @@ def _fused_ref_chain(cp, recv_d, B, W, md):
     (2, 2, 64, 3, 128, True),     # several batches: rows arrive in chunks of S_l
     (2, 4, 128, 2, 128, False),
     (3, 2, 192, 1, 64, True),
+    (1, 4, 1024, 1, 128, False),  # 32 query blocks: split-KV, strided views
+    (2, 2, 2048, 1, 128, True),   # 64 query blocks: split-KV, chunked rows
 ])
 def test_recv_to_send_matches_oracle_and_unfused(gu, B, W, Sl, Hl, D, masked):
     import context_attention_diffusion_amd as cp
@@ -367,6 +369,7 @@ def test_chunked_kv_arrival_full_size_sampled(gu):
     (1, 1, 33, 64, 1, 128, True, True, False),        # one joint key
     (2, 2, 129, 500, 200, 128, False, False, False),  # no masks
     (1, 2, 64, 300, 0, 64, False, True, False),       # no joint tokens
+    (1, 1, 256, 4096, 77, 128, True, False, True),    # 2 query blocks: split-KV over two segments
 ])
 def test_joint_segments_match_oracle(gu, B, H, Sq, S_img, T, D, front, im_on, jm_on):
     import context_attention_diffusion_amd as cp

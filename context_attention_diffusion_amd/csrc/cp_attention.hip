@@ -736,22 +736,28 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       }
       return;
     }
-    if (q_row < a.Sq) {
-      __bf16* op = a.o + b * a.ov.bs + row_off_t<kChunked>(a.ov, q_row) + h * a.ov.hs;
-      // Accumulator row r of block db is d = db*32 + 8*(r/4) + 4*hi + r%4.
+    // Accumulator row r of block db is d = db*32 + 8*(r/4) + 4*hi + r%4: lanes l and
+    // l + 32 hold the two 4-element halves of each 8-element run.  One swap per
+    // dword pair hands lane l the run of g = 2k and lane l + 32 that of g = 2k + 1,
+    // so each lane stores 16 contiguous bytes.  (Both lanes of a pair hold the same
+    // query row, so they are valid or not together.)
+    __bf16* op = a.o + b * a.ov.bs + row_off_t<kChunked>(a.ov, q_row < a.Sq ? q_row : 0) + h * a.ov.hs;
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 w;
+      for (int k = 0; k < 2; ++k) {
+        bf16x4 w0, w1;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            w[e] = (__bf16)(acc_o[db][r] * c0 + cb[db][g][e] * c1);
-          }
-          *reinterpret_cast<bf16x4*>(op + db * 32 + 8 * g + 4 * hi) = w;
+        for (int e = 0; e < 4; ++e) {
+          w0[e] = (__bf16)(acc_o[db][8 * k + e] * c0 + cb[db][2 * k][e] * c1);
+          w1[e] = (__bf16)(acc_o[db][8 * k + 4 + e] * c0 + cb[db][2 * k + 1][e] * c1);
         }
-    }
+        const uint2 x = __builtin_bit_cast(uint2, w0), y = __builtin_bit_cast(uint2, w1);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
+        const uint4 out = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+        if (q_row < a.Sq) *reinterpret_cast<uint4*>(op + db * 32 + 8 * (2 * k + hi)) = out;
+      }
   }
   };  // process
 

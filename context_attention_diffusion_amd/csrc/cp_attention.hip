@@ -550,6 +550,11 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       using BQ = std::integral_constant<int, 1 - P>;
       if (i < n_g) {
         const bool nx = i + 1 < n_g;
+        // the Q K^T chains first, so that the matrix pipe starts right after the
+        // barrier; the fills (which can stall at issue while the texture path
+        // drains) follow
+        qk(ktile(I0{}, BP{}), sc);
+        __builtin_amdgcn_sched_barrier(0);
         if (nx) {
           fill(0, 2 * (i0 + i + 1), ktile(I0{}, BQ{}));
           fill(1, 2 * (i0 + i + 1), vtile(I0{}, BQ{}));
@@ -559,7 +564,6 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
         if (i + 2 < n_g1) fill(0, 2 * (i0 + i + 2) + 1, ktile(I1{}, BP{}));
         if (i + 1 < n_g1) fill(1, 2 * (i0 + i + 1) + 1, vtile(I1{}, BQ{}));
         __builtin_amdgcn_sched_barrier(0);
-        qk(ktile(I0{}, BP{}), sc);
         rescale(bias_max(P, tile_of(i), sc));
         prob_pv(vtile(I0{}, BP{}));
         if (nx) store_bias(1 - P);

@@ -304,6 +304,19 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsrc, (lds_void*)(dst + (gw * C::SPT + j) * 1024), 16, goff[j], 0, 0, 0);
   };
+  // The descriptor of tile t (which: 0 = K, 1 = V), and one of its SPT fill
+  // instructions, for spreading a tile's fills over other work.
+  auto fill_rsrc = [&](int which, int t) {
+    bool s1;
+    int key0, len;
+    seg_of(t, s1, key0, len);
+    const int rows = min(C::BN, len - key0);
+    const __bf16* src = s1 ? (which ? vbase1 : kbase1) + (long long)key0 * a.kv.rs
+                           : (which ? vbase : kbase) + row_off_t<kChunked>(a.kv, key0);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(src), (short)0, int(uint32_t(rows - 1) * rs_bytes + uint32_t(D) * 2u),
+        0x00020000);
+  };
   // Tile arrays of key group G, buffer B (both compile-time).
   auto ktile = [&](auto g, auto bf) -> char* {
     constexpr int G = decltype(g)::value, B = decltype(bf)::value;
@@ -504,6 +517,32 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     }
     s[kb] = acc;
   };
+  // Q K^T whose steps are interleaved with up to 16 fill instructions: after step
+  // kk, fills 2kk and 2kk+1 of the list (tile f / 4, instruction f % 4) when that
+  // tile is to be filled.  Scheduling fences keep the fills in place while MFMAs
+  // and LDS reads move freely.
+  auto qk_fills = [&](const char* kt, f32x16* s, const bool* want, const __amdgpu_buffer_rsrc_t* rs,
+                      char* const* dst) {
+    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk) {
+      const bf16x8 kf0 = *reinterpret_cast<const bf16x8*>(kt - kKHigh + kx[kk]);
+      const bf16x8 kf1 = *reinterpret_cast<const bf16x8*>(kt - kKHigh + 32 * C::RB + kx[kk]);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[kk], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[kk], acc1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0x078F);
+#pragma unroll
+      for (int f = 2 * kk; f < 2 * kk + 2; ++f) {
+        const int tile = f / C::SPT, j = f % C::SPT;
+        if (tile < 4 && want[tile])
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[tile], (lds_void*)(dst[tile] + (gw * C::SPT + j) * 1024), 16,
+                                                   goff[j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0x078F);
+    }
+    s[0] = acc0;
+    s[1] = acc1;
+  };
   auto prob_pv = [&](const char* vt) {
     bf16x8 pf[4];
     const float lsum = softmax(sc, -nm_use, pf);
@@ -550,20 +589,20 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       using BQ = std::integral_constant<int, 1 - P>;
       if (i < n_g) {
         const bool nx = i + 1 < n_g;
-        // the Q K^T chains first, so that the matrix pipe starts right after the
-        // barrier; the fills (which can stall at issue while the texture path
-        // drains) follow
-        qk(ktile(I0{}, BP{}), sc);
-        __builtin_amdgcn_sched_barrier(0);
-        if (nx) {
-          fill(0, 2 * (i0 + i + 1), ktile(I0{}, BQ{}));
-          fill(1, 2 * (i0 + i + 1), vtile(I0{}, BQ{}));
-          bias_of(tile_of(i + 1));
+        // the fills of the next tiles (both groups) go out two at a time between the
+        // Q K^T steps: issued at the top of the iteration they held back the first
+        // MFMAs (a fill can stall at issue while the texture path drains); spread
+        // over the chain, their stalls overlap MFMA execution
+        {
+          const bool want[4] = {nx, nx, i + 2 < n_g1, i + 1 < n_g1};
+          const int tl[4] = {2 * (i0 + i + 1), 2 * (i0 + i + 1), 2 * (i0 + i + 2) + 1, 2 * (i0 + i + 1) + 1};
+          const __amdgpu_buffer_rsrc_t rs[4] = {fill_rsrc(0, tl[0]), fill_rsrc(1, tl[1]), fill_rsrc(0, tl[2]),
+                                                fill_rsrc(1, tl[3])};
+          char* const dst[4] = {ktile(I0{}, BQ{}), vtile(I0{}, BQ{}), ktile(I1{}, BP{}), vtile(I1{}, BQ{})};
+          qk_fills(ktile(I0{}, BP{}), sc, want, rs, dst);
         }
-        // group 1's next K (two tiles ahead) and V (one tile ahead)
-        if (i + 2 < n_g1) fill(0, 2 * (i0 + i + 2) + 1, ktile(I1{}, BP{}));
-        if (i + 1 < n_g1) fill(1, 2 * (i0 + i + 1) + 1, vtile(I1{}, BQ{}));
         __builtin_amdgcn_sched_barrier(0);
+        if (nx) bias_of(tile_of(i + 1));
         rescale(bias_max(P, tile_of(i), sc));
         prob_pv(vtile(I0{}, BP{}));
         if (nx) store_bias(1 - P);

@@ -705,7 +705,7 @@ def calib_copy():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the kernels run one rank's share on one GPU; --gpus must be 1 (the exchange is simulated on that GPU)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.summarize_traffic:

@@ -275,7 +275,10 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 
   // ---- HBM -> LDS fill.  Slot s of a tile (16 bytes) holds chunk
   // (s % CHUNKS) ^ swz(key) of row key = s / CHUNKS; instruction j of wave gw
-  // fills slots [(gw*SPT + j)*64, +64), lane-ordered.
+  // fills slots [(gw*SPT + j)*64, +64), lane-ordered.  The SPT instructions of a
+  // wave share one LDS base (the M0 register): instruction j carries its 1 KB step
+  // as the immediate offset, which the hardware adds to both the LDS and the
+  // global address, so the lane offsets are stored 1 KB * j low.
   const uint32_t rs_bytes = uint32_t(a.kv.rs) * 2u;
   uint32_t goff[C::SPT];
 #pragma unroll
@@ -283,8 +286,18 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     const int slot = (gw * C::SPT + j) * 64 + lane;
     const int key = slot / C::CHUNKS;
     const int chunk = (slot % C::CHUNKS) ^ C::swz(key);
-    goff[j] = uint32_t(key) * rs_bytes + uint32_t(chunk) * 16u;
+    goff[j] = uint32_t(key) * rs_bytes + uint32_t(chunk) * 16u - uint32_t(j) * 1024u;
   }
+  static_assert(C::SPT == 2 || C::SPT == 4, "fill instructions per wave");
+  auto fill_j = [&](int j, __amdgpu_buffer_rsrc_t rs, char* dst) {
+    lds_void* const d = (lds_void*)(dst + gw * C::SPT * 1024);
+    switch (j) {
+      case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, goff[0], 0, 0, 0); break;
+      case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, goff[1], 0, 1024, 0); break;
+      case 2: if constexpr (C::SPT > 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, goff[2 % C::SPT], 0, 2048, 0); break;
+      default: if constexpr (C::SPT > 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, goff[3 % C::SPT], 0, 3072, 0); break;
+    }
+  };
   // dst: the destination tile array.
   // The 64 rows of a tile are contiguous at stride rs (a chunked view has chunks
   // of a multiple of 64 rows); rows past the last key are outside the range.
@@ -301,8 +314,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
         0x00020000);
 #pragma unroll
     for (int j = 0; j < C::SPT; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (lds_void*)(dst + (gw * C::SPT + j) * 1024), 16, goff[j], 0, 0, 0);
+      fill_j(j, rsrc, dst);
   };
   // The descriptor of tile t (which: 0 = K, 1 = V), and one of its SPT fill
   // instructions, for spreading a tile's fills over other work.
@@ -518,11 +530,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     s[kb] = acc;
   };
   // Q K^T whose steps are interleaved with up to 16 fill instructions: after step
-  // kk, fills 2kk and 2kk+1 of the list (tile f / 4, instruction f % 4) when that
-  // tile is to be filled.  Scheduling fences keep the fills in place while MFMAs
-  // and LDS reads move freely.
-  auto qk_fills = [&](const char* kt, f32x16* s, const bool* want, const __amdgpu_buffer_rsrc_t* rs,
-                      char* const* dst) {
+  // kk, fills 2kk and 2kk+1 of the list (tile f / SPT, instruction f % SPT).
+  // Scheduling fences keep the fills in place while MFMAs and LDS reads move freely.
+  auto qk_fills = [&](const char* kt, f32x16* s, const __amdgpu_buffer_rsrc_t* rs, char* const* dst) {
     f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < C::KS; ++kk) {
@@ -534,9 +544,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 #pragma unroll
       for (int f = 2 * kk; f < 2 * kk + 2; ++f) {
         const int tile = f / C::SPT, j = f % C::SPT;
-        if (tile < 4 && want[tile])
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[tile], (lds_void*)(dst[tile] + (gw * C::SPT + j) * 1024), 16,
-                                                   goff[j], 0, 0, 0);
+        if (tile < 4) fill_j(j, rs[tile], dst[tile]);
       }
       __builtin_amdgcn_sched_barrier(0x078F);
     }
@@ -592,14 +600,19 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
         // the fills of the next tiles (both groups) go out two at a time between the
         // Q K^T steps: issued at the top of the iteration they held back the first
         // MFMAs (a fill can stall at issue while the texture path drains); spread
-        // over the chain, their stalls overlap MFMA execution
+        // over the chain, their stalls overlap MFMA execution.  They are issued
+        // unconditionally (no branches in the chain): a tile past the end of its
+        // group is replaced by this iteration's tile, re-read into a buffer that
+        // nothing reads before the next fill of it.
         {
           const bool want[4] = {nx, nx, i + 2 < n_g1, i + 1 < n_g1};
-          const int tl[4] = {2 * (i0 + i + 1), 2 * (i0 + i + 1), 2 * (i0 + i + 2) + 1, 2 * (i0 + i + 1) + 1};
+          const int tc = 2 * (i0 + i);
+          const int tl[4] = {want[0] ? 2 * (i0 + i + 1) : tc, want[1] ? 2 * (i0 + i + 1) : tc,
+                             want[2] ? 2 * (i0 + i + 2) + 1 : tc, want[3] ? 2 * (i0 + i + 1) + 1 : tc};
           const __amdgpu_buffer_rsrc_t rs[4] = {fill_rsrc(0, tl[0]), fill_rsrc(1, tl[1]), fill_rsrc(0, tl[2]),
                                                 fill_rsrc(1, tl[3])};
           char* const dst[4] = {ktile(I0{}, BQ{}), vtile(I0{}, BQ{}), ktile(I1{}, BP{}), vtile(I1{}, BQ{})};
-          qk_fills(ktile(I0{}, BP{}), sc, want, rs, dst);
+          qk_fills(ktile(I0{}, BP{}), sc, rs, dst);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (nx) bias_of(tile_of(i + 1));

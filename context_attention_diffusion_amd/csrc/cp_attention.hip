@@ -110,10 +110,34 @@ __device__ __forceinline__ float max2(float a, float b) {
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+// Maximum of the 32 scores of two accumulator blocks, as two instruction blocks (the
+// compiler pads every inline-assembly boundary with a wait state, so it sees two
+// boundaries instead of one per v_max3).
+__device__ __forceinline__ float max_of_32(const f32x16& x, const f32x16& y) {
+  float m;
+  asm("v_max3_f32 %0, %1, %2, %3\n\t"
+      "v_max3_f32 %0, %0, %4, %5\n\t"
+      "v_max3_f32 %0, %0, %6, %7\n\t"
+      "v_max3_f32 %0, %0, %8, %9\n\t"
+      "v_max3_f32 %0, %0, %10, %11\n\t"
+      "v_max3_f32 %0, %0, %12, %13\n\t"
+      "v_max3_f32 %0, %0, %14, %15\n\t"
+      "v_max3_f32 %0, %0, %16, %17"
+      : "=&v"(m)
+      : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]), "v"(x[8]),
+        "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]), "v"(y[0]));
+  asm("v_max3_f32 %0, %0, %1, %2\n\t"
+      "v_max3_f32 %0, %0, %3, %4\n\t"
+      "v_max3_f32 %0, %0, %5, %6\n\t"
+      "v_max3_f32 %0, %0, %7, %8\n\t"
+      "v_max3_f32 %0, %0, %9, %10\n\t"
+      "v_max3_f32 %0, %0, %11, %12\n\t"
+      "v_max3_f32 %0, %0, %13, %14\n\t"
+      "v_max_f32 %0, %0, %15"
+      : "+v"(m)
+      : "v"(y[1]), "v"(y[2]), "v"(y[3]), "v"(y[4]), "v"(y[5]), "v"(y[6]), "v"(y[7]), "v"(y[8]), "v"(y[9]),
+        "v"(y[10]), "v"(y[11]), "v"(y[12]), "v"(y[13]), "v"(y[14]), "v"(y[15]));
+  return m;
 }
 __device__ __forceinline__ float pair_max(float x) {
   float u, w;
@@ -424,13 +448,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
           s[kb][4 * g + 3] += bb.w;
         }
     }
-    float mx = max3(s[0][0], s[0][1], s[0][2]);
-#pragma unroll
-    for (int r = 3; r < 15; r += 2) mx = max3(mx, s[0][r], s[0][r + 1]);
-    mx = max3(mx, s[0][15], s[1][0]);
-#pragma unroll
-    for (int r = 1; r < 16; r += 2) mx = max3(mx, s[1][r], s[1][r + 1 < 16 ? r + 1 : r]);
-    return pair_max(mx) * a.sc;
+    return pair_max(max_of_32(s[0], s[1])) * a.sc;
   };
   // Probabilities in B-operand order (step m uses block m/2, rows 8*(m%2) .. +8)
   // and their bf16 sum.

@@ -231,7 +231,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // read takes its tile base as an immediate instead of an address add.
   __shared__ __attribute__((aligned(1024))) char lds0_v00[C::TILE], lds0_v01[C::TILE], lds0_v10[C::TILE], lds0_v11[C::TILE];
   __shared__ __attribute__((aligned(1024))) char lds1_k00[C::TILE], lds1_k01[C::TILE], lds1_k10[C::TILE], lds1_k11[C::TILE];
-  __shared__ __attribute__((aligned(16))) float lds2_bias[kGroups * 2 * C::BN];
+  __shared__ __attribute__((aligned(16))) float lds2_bias[6 * C::BN];
 
   const int tid = threadIdx.x;
   // Wave-uniform indices go through readfirstlane so that the compiler keeps
@@ -365,6 +365,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   const int n_g1 = tiles_of_group(1);  // tiles of group 1 (local tile i is global tile 2(i0 + i) + 1)
+  // Bias rows: group 0 keeps tile i's row in slot i % 2, group 1 in slot i % 4 (it
+  // reads a row one iteration later, at the top of the iteration that uses it, so a
+  // row is rewritten only after a barrier has followed its last read).
   float* bias_row = lds2_bias + grp * 2 * C::BN;
 
   // Key validity of tile t as an additive bias, one key per thread of wave 0.
@@ -577,7 +580,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   };
 
   // ---- prologue.  Group 0 consumes K and V of tile i in iteration i; group 1
-  // runs one K tile ahead (its iteration i ends with the scores of tile i+1).
+  // runs one K tile ahead (its iteration i ends with the scores of tile i+1, whose
+  // max it takes at the top of iteration i+1, while group 0 is in its Q K^T).
   // Only group 0 issues HBM->LDS fills, for both groups' buffers: fill
   // instructions stall at issue while the texture path drains, and group 1 is
   // the one on the critical path.
@@ -599,6 +603,10 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   if (grp == 1 && n_g > 1) {
     bias_of(tile_of(1));
     store_bias(1);
+  }
+  if (grp == 1 && n_g > 2) {
+    bias_of(tile_of(2));
+    store_bias(2);
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's LDS fills have landed
   __syncthreads();
@@ -648,16 +656,18 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   } else {
     if (n_g > 0) {
       qk(ktile(I1{}, I0{}), sc);
-      m_run = bias_max(0, tile_of(0), sc);
-      nm_use = m_run == -INFINITY ? 0.f : -m_run;
     }
     auto iter1 = [&](auto par, int i) {
       constexpr int P = decltype(par)::value;
       using BP = std::integral_constant<int, P>;
       using BQ = std::integral_constant<int, 1 - P>;
       if (i < n_g) {
-        const bool nx = i + 1 < n_g, nk = i + 2 < n_g;
-        if (nk) bias_of(tile_of(i + 2));
+        const bool nk = i + 3 < n_g;
+        if (nk) bias_of(tile_of(i + 3));
+        // tile i's max: its scores were finished by the previous iteration; taken
+        // here, after the barrier, it overlaps group 0's Q K^T instead of delaying
+        // this group's arrival at the barrier
+        rescale(bias_max(i & 3, tile_of(i), sc));
         __builtin_amdgcn_sched_barrier(0);
         // tile i's softmax and P V in two halves, each followed by the matching half
         // of tile i+1's Q K^T (computed unconditionally: on the last tile it reads an
@@ -673,8 +683,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
           l_run += lsum;
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (nx) rescale(bias_max(1 - P, tile_of(i + 1), sc));
-        if (nk) store_bias(P);
+        if (nk) store_bias((i + 3) & 3);
       }
       __builtin_amdgcn_s_waitcnt(0x0f70);
       __syncthreads();

@@ -509,9 +509,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       nm_use = m_run == -INFINITY ? 0.f : -m_run;
     }
   };
-  // Half-tile pieces (keys 32*kb .. 32*kb + 31) of the softmax, the P V product
-  // and the Q K^T chain, for interleaving one tile's second half with the next
-  // tile's first.
+  // Half-tile pieces (keys 32*kb .. 32*kb + 31) of the softmax and the P V
+  // product: group 1 runs each half's P V right after that half's softmax.
   auto softmax_part = [&](const f32x16* s, int kb, bf16x8* pf) -> float {
     float lsum = 0.f;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -540,15 +539,6 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[m], acc_o[db], 0, 0, 0);
       }
-  };
-  auto qk_part = [&](const char* kt, f32x16* s, int kb) {
-    f32x16 acc = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < C::KS; ++kk) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt - kKHigh + kb * 32 * C::RB + kx[kk]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc, 0, 0, 0);
-    }
-    s[kb] = acc;
   };
   // Q K^T whose steps are interleaved with up to 16 fill instructions: after step
   // kk, fills 2kk and 2kk+1 of the list (tile f / SPT, instruction f % SPT).
@@ -669,17 +659,18 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
         // this group's arrival at the barrier
         rescale(bias_max(i & 3, tile_of(i), sc));
         __builtin_amdgcn_sched_barrier(0);
-        // tile i's softmax and P V in two halves, each followed by the matching half
-        // of tile i+1's Q K^T (computed unconditionally: on the last tile it reads an
-        // idle buffer and is discarded)
+        // tile i's softmax and P V in two halves, then tile i+1's Q K^T as two
+        // interleaved chains (computed unconditionally: on the last tile it reads an
+        // idle buffer and is discarded).  The second half's softmax then runs while
+        // group 0 is in its P V MFMAs, and this group's Q K^T while group 0 waits
+        // for its fills.
         {
           bf16x8 pf[4];
           float lsum = softmax_part(sc, 0, pf);
           pv_part(vtile(I1{}, BP{}), pf, 0);
-          qk_part(ktile(I1{}, BQ{}), sc, 0);
           lsum += softmax_part(sc, 1, pf);
           pv_part(vtile(I1{}, BP{}), pf, 1);
-          qk_part(ktile(I1{}, BQ{}), sc, 1);
+          qk(ktile(I1{}, BQ{}), sc);
           l_run += lsum;
         }
         __builtin_amdgcn_sched_barrier(0);

@@ -453,41 +453,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     }
     return pair_max(max_of_32(s[0], s[1])) * a.sc;
   };
-  // Probabilities in B-operand order (step m uses block m/2, rows 8*(m%2) .. +8)
-  // and their bf16 sum.
-  auto softmax = [&](const f32x16* s, float m_use, bf16x8* pf) -> float {
-    float lsum = 0.f;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        pf[m][kk] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[m >> 1][8 * (m & 1) + kk], a.sc, -m_use));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x2 pr = {pf[m][2 * j], pf[m][2 * j + 1]};
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
-      }
-    }
-    return lsum;
-  };
   f32x16 acc_o[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc_o[db] = f32x16{};
-  // O^T[d][query] += V^T[d][keys] P^T[keys][query]
-  auto pv = [&](const char* vt, const bf16x8* pf) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const i16x4 lo =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + 16 * m * C::RB + (vaddr0 ^ (db * 64))));
-        const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vt + (16 * m + 8) * C::RB + (vaddr1 ^ (db * 64))));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[m], acc_o[db], 0, 0, 0);
-      }
-  };
 
   float m_run = -INFINITY;  // running max, scaled log2 units (shared by lanes l, l^32)
   float nm_use = 0.f;       // -m_run, or 0 while m_run is -inf (the softmax's offset)
@@ -510,7 +478,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     }
   };
   // Half-tile pieces (keys 32*kb .. 32*kb + 31) of the softmax and the P V
-  // product: group 1 runs each half's P V right after that half's softmax.
+  // product; both groups run each half's P V right after that half's softmax.
+  // Probabilities go to B-operand order (step m uses block m/2, rows 8*(m%2) .. +8),
+  // and the bf16 values are summed; O^T[d][query] += V^T[d][keys] P^T[keys][query].
   auto softmax_part = [&](const f32x16* s, int kb, bf16x8* pf) -> float {
     float lsum = 0.f;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -561,12 +531,6 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     }
     s[0] = acc0;
     s[1] = acc1;
-  };
-  auto prob_pv = [&](const char* vt) {
-    bf16x8 pf[4];
-    const float lsum = softmax(sc, -nm_use, pf);
-    pv(vt, pf);
-    l_run += lsum;
   };
 
   // ---- prologue.  Group 0 consumes K and V of tile i in iteration i; group 1
@@ -633,7 +597,14 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
         __builtin_amdgcn_sched_barrier(0);
         if (nx) bias_of(tile_of(i + 1));
         rescale(bias_max(P, tile_of(i), sc));
-        prob_pv(vtile(I0{}, BP{}));
+        {
+          bf16x8 pf[4];
+          float lsum = softmax_part(sc, 0, pf);
+          pv_part(vtile(I0{}, BP{}), pf, 0);
+          lsum += softmax_part(sc, 1, pf);
+          pv_part(vtile(I0{}, BP{}), pf, 1);
+          l_run += lsum;
+        }
         if (nx) store_bias(1 - P);
       }
       __builtin_amdgcn_s_waitcnt(0x0f70);

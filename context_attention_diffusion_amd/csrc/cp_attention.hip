@@ -511,8 +511,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       }
   };
   // Q K^T whose steps are interleaved with up to 16 fill instructions: after step
-  // kk, fills 2kk and 2kk+1 of the list (tile f / SPT, instruction f % SPT).
-  // Scheduling fences keep the fills in place while MFMAs and LDS reads move freely.
+  // kk, fills 3kk .. 3kk+2 of the list (tile f / SPT, instruction f % SPT), so the
+  // last ones go out by two thirds of the chain.  Scheduling fences keep the fills
+  // in place while MFMAs and LDS reads move freely.
   auto qk_fills = [&](const char* kt, f32x16* s, const __amdgpu_buffer_rsrc_t* rs, char* const* dst) {
     f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
@@ -523,7 +524,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[kk], acc1, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0x078F);
 #pragma unroll
-      for (int f = 2 * kk; f < 2 * kk + 2; ++f) {
+      for (int f = 3 * kk; f < 3 * kk + 3 && f < 4 * C::SPT; ++f) {
         const int tile = f / C::SPT, j = f % C::SPT;
         if (tile < 4) fill_j(j, rs[tile], dst[tile]);
       }
@@ -577,10 +578,11 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       using BQ = std::integral_constant<int, 1 - P>;
       if (i < n_g) {
         const bool nx = i + 1 < n_g;
-        // the fills of the next tiles (both groups) go out two at a time between the
-        // Q K^T steps: issued at the top of the iteration they held back the first
+        // the fills of the next tiles (both groups) go out three at a time between
+        // the Q K^T steps: issued at the top of the iteration they held back the first
         // MFMAs (a fill can stall at issue while the texture path drains); spread
-        // over the chain, their stalls overlap MFMA execution.  They are issued
+        // over the chain, their stalls overlap MFMA execution.  Group 1's V tile,
+        // which it reads first in the next iteration, goes first.  They are issued
         // unconditionally (no branches in the chain): a tile past the end of its
         // group is replaced by this iteration's tile, re-read into a buffer that
         // nothing reads before the next fill of it.
@@ -589,9 +591,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
           const int tc = 2 * (i0 + i);
           const int tl[4] = {want[0] ? 2 * (i0 + i + 1) : tc, want[1] ? 2 * (i0 + i + 1) : tc,
                              want[2] ? 2 * (i0 + i + 2) + 1 : tc, want[3] ? 2 * (i0 + i + 1) + 1 : tc};
-          const __amdgpu_buffer_rsrc_t rs[4] = {fill_rsrc(0, tl[0]), fill_rsrc(1, tl[1]), fill_rsrc(0, tl[2]),
-                                                fill_rsrc(1, tl[3])};
-          char* const dst[4] = {ktile(I0{}, BQ{}), vtile(I0{}, BQ{}), ktile(I1{}, BP{}), vtile(I1{}, BQ{})};
+          const __amdgpu_buffer_rsrc_t rs[4] = {fill_rsrc(1, tl[3]), fill_rsrc(0, tl[0]), fill_rsrc(1, tl[1]),
+                                                fill_rsrc(0, tl[2])};
+          char* const dst[4] = {vtile(I1{}, BQ{}), ktile(I0{}, BQ{}), vtile(I0{}, BQ{}), ktile(I1{}, BP{})};
           qk_fills(ktile(I0{}, BP{}), sc, rs, dst);
         }
         __builtin_amdgcn_sched_barrier(0);

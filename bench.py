@@ -77,6 +77,10 @@ def parse():
     p.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench and of "
                         "--calib-copy into a traffic summary; no GPU work")
+    p.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "OUT_MD"),
+                   help="turn one rocprofv3 --pmc run of this bench (SQ_VALU_MFMA_BUSY_CYCLES, "
+                        "SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_BUSY_CU_CYCLES, GRBM_GUI_ACTIVE) into an MFMA "
+                        "utilisation summary of the attention kernel; no GPU work")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the fused-chain, chunked-K/V and joint-segment sections (so a kernel "
                         "trace of the run holds only the headline step's launches)")
@@ -692,6 +696,64 @@ def summarize_traffic(fetch_dir, write_dir, out_json, workload):
     print(json.dumps(res))
 
 
+def summarize_mfma(pmc_dir, out_md, workload):
+    """MFMA utilisation of the attention kernel from one counter run: matrix-core busy cycles
+    over (active cycles x SIMDs), the bf16 MFMA work the counters saw (512 flops per MOP)
+    against the algorithmic count, and the share of CU-cycles with a workgroup resident."""
+    import csv
+    import glob
+    import workloads
+    wl = workloads.WORKLOADS[workload]
+    n_xcd = 8
+    n_cu = 256
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*agent_info.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Agent_Type", r.get("Type", "")).upper().endswith("GPU") or r.get("Name", "").startswith("gfx"):
+                n_xcd = int(float(r.get("Num_Xcc", r.get("num_xcc", n_xcd)) or n_xcd))
+                n_cu = int(float(r.get("Cu_Count", r.get("cu_count", n_cu)) or n_cu))
+    busy = read_counter_csv(pmc_dir, "SQ_VALU_MFMA_BUSY_CYCLES", "attn_fwd")
+    mops = read_counter_csv(pmc_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16", "attn_fwd")
+    cu_busy = read_counter_csv(pmc_dir, "SQ_BUSY_CU_CYCLES", "attn_fwd")
+    gui = read_counter_csv(pmc_dir, "GRBM_GUI_ACTIVE", "attn_fwd")
+    cycles = gui / n_xcd                      # the counter is summed over the XCDs
+    simds = 4 * n_cu
+    flops_ctr = mops * 512.0
+    flops_alg = float(wl.attn_flops_dense())
+    lines = [
+        f"# MFMA utilisation: attention kernel, workload {workload}",
+        "",
+        "Command (repository root, one MI355X):",
+        "",
+        "```",
+        f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE "
+        f"-d {pmc_dir} -o p --output-format csv -- python3 bench.py --workload {workload} --only attn --steps 5 "
+        f"--warmup 1 --eager --no-cold --no-cpu-baseline",
+        f"python3 bench.py --workload {workload} --summarize-mfma {pmc_dir} {out_md}",
+        "```",
+        "",
+        f"Per attn_fwd_kernel dispatch (mean over the dispatches of the run; {n_xcd} XCDs, {n_cu} CUs, "
+        f"{simds} SIMDs; the profiler serialises dispatches):",
+        "",
+        "| quantity | value |",
+        "|---|---|",
+        f"| active cycles (GRBM_GUI_ACTIVE / XCDs) | {cycles:.0f} |",
+        f"| matrix-core busy cycles, all SIMDs (SQ_VALU_MFMA_BUSY_CYCLES) | {busy:.4g} |",
+        f"| MFMA utilisation = busy / (active cycles x SIMDs) | {100.0 * busy / (cycles * simds):.1f}% |",
+        f"| CU-cycles with a workgroup resident (SQ_BUSY_CU_CYCLES / (active cycles x CUs)) | "
+        f"{100.0 * cu_busy / (cycles * n_cu):.1f}% |",
+        f"| MFMA utilisation of the resident CUs = busy / (4 x SQ_BUSY_CU_CYCLES) | {100.0 * busy / (4.0 * cu_busy):.1f}% |",
+        f"| bf16 MFMA flops counted (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) | {flops_ctr:.6g} |",
+        f"| algorithmic flops (4 B H Sq Skv D) | {flops_alg:.6g} |",
+        "",
+        "Busy cycles count the matrix pipe of a SIMD while it executes an MFMA; at the 2.5 PFLOP/s dense "
+        "bf16 peak every SIMD would be busy every cycle, so the utilisation here is the fraction of that peak "
+        "the kernel reaches at the clock it ran at.",
+    ]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def calib_copy():
     import torch
     a = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda:0").normal_()
@@ -710,6 +772,9 @@ def main():
         sys.exit(2)
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.workload)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma, args.workload)
         return
     import torch
 

@@ -37,8 +37,9 @@ received buffer and writes the send layout directly.
 Prints one JSON line.  `value` is attention TFLOP/s over the whole step
 (algorithmic attention FLOPs / step time), with the step captured once into a
 HIP graph and replayed (`--eager` launches it op by op).  Per-kernel durations
-come from HIP events on the launch stream around a HIP-graph replay of a burst
-of back-to-back launches of each kernel on the step's own buffers.
+come from HIP events on the launch stream around HIP-graph replays of a burst
+of up to 100 back-to-back launches of each kernel on the step's own buffers
+(three warm-up launches, one untimed replay, the median of three timed ones).
 """
 
 from __future__ import annotations
@@ -361,12 +362,14 @@ def parity_sample(path, wl, nrows=24):
     return res
 
 
-def time_burst(fn, burst):
-    """Average duration (ms) of `fn` over `burst` back-to-back launches: the burst is
-    captured once into a HIP graph and its replay is timed with HIP events on the
-    launch stream, so host launch overhead does not enter the figure."""
+def time_burst(fn, burst, repeats=3):
+    """Duration (ms) of one launch of `fn`: three warm-up launches, then `burst` back-to-back
+    launches captured once into a HIP graph, replayed once untimed and `repeats` times
+    timed with HIP events on the launch stream; the median replay over `burst`.  Host
+    launch overhead does not enter the figure."""
     import torch
-    fn()
+    for _ in range(3):
+        fn()
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -374,13 +377,16 @@ def time_burst(fn, burst):
             fn()
     graph.replay()
     torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    s.record()
-    graph.replay()
-    e.record()
-    torch.cuda.synchronize()
-    return s.elapsed_time(e) / burst
+    times = []
+    for _ in range(repeats):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        graph.replay()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e) / burst)
+    return float(np.median(times))
 
 
 def kernel_bursts(path, only=None, burst=20):
@@ -825,8 +831,8 @@ def main():
 
     # Per-kernel durations: each kernel of the step launched `burst` times back to
     # back on the launch stream between one pair of HIP events (same buffers as the
-    # step), so the event overhead is amortised.
-    kms = kernel_bursts(path, only=args.only, burst=max(5, min(50, args.steps)))
+    # step), three timed replays, the median kept.
+    kms = kernel_bursts(path, only=args.only, burst=max(5, min(100, args.steps)))
 
     flops = attn_flops(wl, path.mask_np)
     pack_bytes, merge_bytes = wl.pack_bytes(), wl.merge_bytes()

@@ -29,10 +29,15 @@
 //    four consecutive keys of one head-dim column; two such reads cover the
 //    eight keys a lane contributes to one MFMA step, in the order the
 //    accumulator layout delivers the matching probabilities.
-//  * Software pipeline per wave: iteration i issues the Q K^T MFMAs of its
-//    next tile while the VALU turns the current tile's scores into
-//    probabilities, then the P V MFMAs of the current tile while the VALU takes
-//    the next tile's row max.  K therefore runs one tile ahead of V in LDS.
+//  * Schedule: each SIMD runs one wave of each group, phase-shifted.  Group 0's
+//    iteration i runs tile i's Q K^T as two interleaved MFMA chains, with the
+//    HBM->LDS fills of the next tiles (of both groups) issued between its steps,
+//    then the tile max, then softmax and P V in two 32-key halves.  Group 1 runs
+//    one K tile ahead: its iteration i takes tile i's max (scores computed the
+//    iteration before), softmax and P V in halves, then tile i+1's Q K^T.  After
+//    each barrier group 0 is in MFMAs while group 1 is in VALU work, and the
+//    roles alternate.  One barrier per iteration publishes the fills and frees
+//    the buffers they overwrite.
 //  * Online softmax in fp32 with exp2 (scale * log2 e folded into one FMA).  The
 //    running max is only raised when a tile's max exceeds it by more than 8 (a
 //    factor 2^8 in probability), so the O rescale is rare; numerator and

@@ -169,9 +169,12 @@ struct View {
   FastDiv L;       // rows per chunk
 };
 
-// Kernel variants (compile-time): chunked row views, and a second key segment.
+// Kernel variants (compile-time): chunked row views, a second key segment, and
+// (with chunked views only) K/V chunks whose row count is not a multiple of the
+// 64-key tile, so that a tile can span chunks.
 constexpr int kModeChunked = 1;
 constexpr int kModeTwoSeg = 2;
+constexpr int kModeCross = 4;
 
 // CHUNKED = false: every view of the kernel is plain.  CHUNKED = true: a view may
 // be chunked (each view says whether it is).
@@ -227,6 +230,8 @@ template <int D, int MODE>
 __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   constexpr bool kChunked = (MODE & kModeChunked) != 0;
   constexpr bool kTwoSeg = (MODE & kModeTwoSeg) != 0;
+  constexpr bool kCross = (MODE & kModeCross) != 0;
+  static_assert(!kCross || kChunked, "tiles cross chunks only in chunked views");
   using C = Cfg<D>;
   // K and V tiles: one array per (operand, key group, buffer).  Separate objects
   // let the compiler see that a fill of one buffer does not alias the reads of
@@ -318,45 +323,77 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     goff[j] = uint32_t(key) * rs_bytes + uint32_t(chunk) * 16u - uint32_t(j) * 1024u;
   }
   static_assert(C::SPT == 2 || C::SPT == 4, "fill instructions per wave");
-  auto fill_j = [&](int j, __amdgpu_buffer_rsrc_t rs, char* dst) {
+  // off: the lane offset of instruction j (goff[j], or xoff for a tile that
+  // spans chunks).
+  auto fill_j = [&](int j, __amdgpu_buffer_rsrc_t rs, char* dst, uint32_t off) {
     lds_void* const d = (lds_void*)(dst + gw * C::SPT * 1024);
     switch (j) {
-      case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, goff[0], 0, 0, 0); break;
-      case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, goff[1], 0, 1024, 0); break;
-      case 2: if constexpr (C::SPT > 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, goff[2 % C::SPT], 0, 2048, 0); break;
-      default: if constexpr (C::SPT > 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, goff[3 % C::SPT], 0, 3072, 0); break;
+      case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, off, 0, 0, 0); break;
+      case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, off, 0, 1024, 0); break;
+      case 2: if constexpr (C::SPT > 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, off, 0, 2048, 0); break;
+      default: if constexpr (C::SPT > 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, off, 0, 3072, 0); break;
     }
   };
-  // dst: the destination tile array.
-  // The 64 rows of a tile are contiguous at stride rs (a chunked view has chunks
-  // of a multiple of 64 rows); rows past the last key are outside the range.
-  // which: 0 = K, 1 = V.
-  auto fill = [&](int which, int t, char* dst) {
-    bool s1;
-    int key0, len;
-    seg_of(t, s1, key0, len);
-    const int rows = min(C::BN, len - key0);
-    const __bf16* src = s1 ? (which ? vbase1 : kbase1) + (long long)key0 * a.kv.rs
-                           : (which ? vbase : kbase) + row_off_t<kChunked>(a.kv, key0);
-    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16*>(src), (short)0, int(uint32_t(rows - 1) * rs_bytes + uint32_t(D) * 2u),
-        0x00020000);
-#pragma unroll
-    for (int j = 0; j < C::SPT; ++j)
-      fill_j(j, rsrc, dst);
+  // A tile of a chunked view whose chunks are not a multiple of 64 rows can span
+  // two or more chunks: its rows are then not at one stride from the tile's first
+  // row.  Such a tile takes per-lane offsets row_off(key0 + key) - row_off(key0)
+  // (rows past the last key get an offset outside the range and read as zero) and
+  // a range up to its last row.
+  auto crosses = [&](int key0, int rows) -> bool {
+    if constexpr (!kCross) {
+      (void)key0;
+      (void)rows;
+      return false;
+    } else {
+      uint32_t c, r;
+      a.kv.L.divmod(uint32_t(key0), c, r);
+      return int(r) + rows > int(a.kv.L.d);
+    }
   };
-  // The descriptor of tile t (which: 0 = K, 1 = V), and one of its SPT fill
-  // instructions, for spreading a tile's fills over other work.
-  auto fill_rsrc = [&](int which, int t) {
+  auto xoff = [&](int j, int key0, int rows) -> uint32_t {
+    const int slot = (gw * C::SPT + j) * 64 + lane;
+    const int key = slot / C::CHUNKS;
+    const int chunk = (slot % C::CHUNKS) ^ C::swz(key);
+    if (key >= rows) return 0x80000000u;
+    const long long dr = row_off_t<true>(a.kv, key0 + key) - row_off_t<true>(a.kv, key0);
+    return uint32_t(dr) * 2u + uint32_t(chunk) * 16u - uint32_t(j) * 1024u;
+  };
+  auto tile_bytes = [&](int key0, int rows, bool cr) -> int {
+    if (kCross && cr) {
+      const long long last = row_off_t<true>(a.kv, key0 + rows - 1) - row_off_t<true>(a.kv, key0);
+      return int(uint32_t(last) * 2u + uint32_t(D) * 2u);
+    }
+    return int(uint32_t(rows - 1) * rs_bytes + uint32_t(D) * 2u);
+  };
+  // The source of tile t (which: 0 = K, 1 = V): its buffer descriptor, and for a
+  // tile that spans chunks its first key and row count.  The 64 rows of a tile are
+  // otherwise contiguous at stride rs; rows past the last key are outside the range.
+  struct FillSrc {
+    __amdgpu_buffer_rsrc_t rs;
+    int key0, rows;
+    bool cross;
+  };
+  auto fill_src = [&](int which, int t) -> FillSrc {
     bool s1;
     int key0, len;
     seg_of(t, s1, key0, len);
     const int rows = min(C::BN, len - key0);
+    const bool cr = !s1 && crosses(key0, rows);
     const __bf16* src = s1 ? (which ? vbase1 : kbase1) + (long long)key0 * a.kv.rs
                            : (which ? vbase : kbase) + row_off_t<kChunked>(a.kv, key0);
-    return __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16*>(src), (short)0, int(uint32_t(rows - 1) * rs_bytes + uint32_t(D) * 2u),
-        0x00020000);
+    return {__builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(src), (short)0, tile_bytes(key0, rows, cr),
+                                              0x00020000),
+            key0, rows, cr};
+  };
+  // Instruction j of a tile's fill into the tile array dst.
+  auto fill_one = [&](const FillSrc& f, int j, char* dst) {
+    fill_j(j, f.rs, dst, (kCross && f.cross) ? xoff(j, f.key0, f.rows) : goff[j]);
+  };
+  // A whole tile.
+  auto fill = [&](int which, int t, char* dst) {
+    const FillSrc f = fill_src(which, t);
+#pragma unroll
+    for (int j = 0; j < C::SPT; ++j) fill_one(f, j, dst);
   };
   // Tile arrays of key group G, buffer B (both compile-time).
   auto ktile = [&](auto g, auto bf) -> char* {
@@ -519,7 +556,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // kk, fills 3kk .. 3kk+2 of the list (tile f / SPT, instruction f % SPT), so the
   // last ones go out by two thirds of the chain.  Scheduling fences keep the fills
   // in place while MFMAs and LDS reads move freely.
-  auto qk_fills = [&](const char* kt, f32x16* s, const __amdgpu_buffer_rsrc_t* rs, char* const* dst) {
+  auto qk_fills = [&](const char* kt, f32x16* s, const FillSrc* fs, char* const* dst) {
     f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < C::KS; ++kk) {
@@ -531,7 +568,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 #pragma unroll
       for (int f = 3 * kk; f < 3 * kk + 3 && f < 4 * C::SPT; ++f) {
         const int tile = f / C::SPT, j = f % C::SPT;
-        if (tile < 4) fill_j(j, rs[tile], dst[tile]);
+        if (tile < 4) fill_one(fs[tile], j, dst[tile]);
       }
       __builtin_amdgcn_sched_barrier(0x078F);
     }
@@ -596,10 +633,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
           const int tc = 2 * (i0 + i);
           const int tl[4] = {want[0] ? 2 * (i0 + i + 1) : tc, want[1] ? 2 * (i0 + i + 1) : tc,
                              want[2] ? 2 * (i0 + i + 2) + 1 : tc, want[3] ? 2 * (i0 + i + 1) + 1 : tc};
-          const __amdgpu_buffer_rsrc_t rs[4] = {fill_rsrc(1, tl[3]), fill_rsrc(0, tl[0]), fill_rsrc(1, tl[1]),
-                                                fill_rsrc(0, tl[2])};
+          const FillSrc fs[4] = {fill_src(1, tl[3]), fill_src(0, tl[0]), fill_src(1, tl[1]), fill_src(0, tl[2])};
           char* const dst[4] = {vtile(I1{}, BQ{}), ktile(I0{}, BQ{}), vtile(I0{}, BQ{}), ktile(I1{}, BP{})};
-          qk_fills(ktile(I0{}, BP{}), sc, rs, dst);
+          qk_fills(ktile(I0{}, BP{}), sc, fs, dst);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (nx) bias_of(tile_of(i + 1));
@@ -1021,17 +1057,20 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
   // combine: BM * D / 4 threads of 256 per query block
   const dim3 grid{unsigned(n_work * args.nsplit)}, block{unsigned(kThreads)}, cblock{256u},
       cgrid{unsigned(n_work * (D / 8))};
-  const int mode = (kv.chunked || qv.chunked || ov.chunked ? kModeChunked : 0) | (Skv1 > 0 ? kModeTwoSeg : 0);
-  if (mode == kModeChunked + kModeTwoSeg) return CP_ERR_UNSUPPORTED;  // no entry point combines them
+  const int mode = (kv.chunked || qv.chunked || ov.chunked ? kModeChunked : 0) | (Skv1 > 0 ? kModeTwoSeg : 0) |
+                   (kv.chunked && kv.L.d % 64 != 0 ? kModeCross : 0);
+  if ((mode & kModeTwoSeg) && (mode & kModeChunked)) return CP_ERR_UNSUPPORTED;  // no entry point combines them
   auto launch_fwd = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, args); };
   if (D == 128) {
     if (mode == 0) launch_fwd(attn_fwd_kernel<128, 0>);
     else if (mode == kModeChunked) launch_fwd(attn_fwd_kernel<128, kModeChunked>);
+    else if (mode == kModeChunked + kModeCross) launch_fwd(attn_fwd_kernel<128, kModeChunked + kModeCross>);
     else launch_fwd(attn_fwd_kernel<128, kModeTwoSeg>);
     if (args.nsplit > 1) hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, cblock, 0, s, args);
   } else {
     if (mode == 0) launch_fwd(attn_fwd_kernel<64, 0>);
     else if (mode == kModeChunked) launch_fwd(attn_fwd_kernel<64, kModeChunked>);
+    else if (mode == kModeChunked + kModeCross) launch_fwd(attn_fwd_kernel<64, kModeChunked + kModeCross>);
     else launch_fwd(attn_fwd_kernel<64, kModeTwoSeg>);
     if (args.nsplit > 1) hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, cblock, 0, s, args);
   }
@@ -1149,8 +1188,9 @@ extern "C" int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, v
   if (B > kIntMax || S > kIntMax - 64 || H_local > kIntMax) return CP_ERR_SHAPE;
   if (H_local * 3 * D * 2 * 64 > kIntMax) return CP_ERR_SHAPE;
   // With several batches the received rows of one batch come in W chunks of
-  // S_local rows; K/V tiles of 64 rows must not straddle two chunks.
-  if (B > 1 && S_local % 64 != 0) return CP_ERR_UNSUPPORTED;
+  // S_local rows.  When S_local is not a multiple of 64 a K/V tile can span
+  // chunks; its lane offsets are then 32-bit differences of row offsets, so the
+  // received buffer must stay below 2 GB.
   const int64_t bm = 32 * kGroupWaves;
   int64_t bh, n_work, re, se;
   if (!mul_capped(B, H_local, kIntMax, &bh) || !mul_capped(bh, (S + bm - 1) / bm, kIntMax, &n_work))
@@ -1158,6 +1198,7 @@ extern "C" int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, v
   if (!mul_capped(B * S, H_local * 3 * D, int64_t(1) << 60, &re)) return CP_ERR_SHAPE;
   se = re / 3;
   const size_t rb = size_t(re) * 2, sb = size_t(se) * 2;
+  if (B > 1 && S_local % 64 != 0 && rb > size_t(kIntMax)) return CP_ERR_SHAPE;
   if (overlaps(send, sb, recv, rb)) return CP_ERR_ALIAS;
   if (key_mask && overlaps(send, sb, key_mask, size_t(B * S))) return CP_ERR_ALIAS;
   const View in = chunked_view(B, S_local, H_local, 3 * D, H_local * 3 * D);

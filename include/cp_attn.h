@@ -334,10 +334,10 @@ int cp_attn_merge(const void* o_parts, const void* lses, int64_t N, void* o,
  *               cp_attn_workspace_bytes(B, S, S, H_local, D)), or NULL
  *
  * Requires the attention's conditions (D in {64, 128}, scale, causal == 0),
- * W >= 1, 16-byte aligned pointers, send disjoint from recv and key_mask, and
- * S_local % 64 == 0 when B > 1 (CP_ERR_UNSUPPORTED otherwise: with several
- * batches a batch's rows arrive in W chunks, and a 64-key tile must not span
- * two of them).
+ * W >= 1, 16-byte aligned pointers, send disjoint from recv and key_mask.  With
+ * B > 1 a batch's rows arrive in W chunks of S_local rows; when S_local is not a
+ * multiple of 64, key tiles that span chunks are addressed row by row, which
+ * needs recv to be smaller than 2 GB (CP_ERR_SHAPE otherwise).
  */
 int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, void* send,
                          int64_t B, int64_t S_local, int64_t H_local, int64_t D, int64_t W,

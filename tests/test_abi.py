@@ -250,7 +250,7 @@ def test_attention_ws_rejects(kw, code):
     (dict(ws=A + 5 * BIG + 8, nbytes=1 << 20), _lib.CP_ERR_ALIGNMENT),
     (dict(s=A + 4096), _lib.CP_ERR_ALIAS),                      # send overlaps recv
     (dict(m=A + BIG + 64), _lib.CP_ERR_ALIAS),                  # mask inside send
-    (dict(B=2, Sl=70), _lib.CP_ERR_UNSUPPORTED),                # chunks not a multiple of 64 rows
+    (dict(B=2, Sl=70, Hl=10000), _lib.CP_ERR_SHAPE),           # tiles span chunks, recv over 2 GB
     (dict(ws=A + 5 * BIG, nbytes=16, Sl=2048), _lib.CP_ERR_WORKSPACE),  # 2 heads x 32 blocks split
     (dict(ws=A, nbytes=1 << 30, Sl=2048), _lib.CP_ERR_ALIAS),   # workspace overlaps recv
     (dict(Sl=1 << 30, W=4), _lib.CP_ERR_SHAPE),

@@ -228,6 +228,11 @@ def _fused_ref_chain(cp, recv_d, B, W, md):
     (3, 2, 192, 1, 64, True),
     (1, 4, 1024, 1, 128, False),  # 32 query blocks: split-KV, strided views
     (2, 2, 2048, 1, 128, True),   # 64 query blocks: split-KV, chunked rows
+    (2, 2, 70, 2, 128, True),     # S_l % 64 != 0: key tiles span two source ranks' chunks
+    (3, 3, 100, 1, 64, False),
+    (2, 4, 40, 2, 128, True),     # chunks shorter than a tile: a tile spans up to three chunks
+    (2, 3, 8, 1, 64, True),       # eight-row chunks
+    (2, 2, 1000, 1, 128, False),  # 32 query blocks with spanning tiles: split-KV
 ])
 def test_recv_to_send_matches_oracle_and_unfused(gu, B, W, Sl, Hl, D, masked):
     import context_attention_diffusion_amd as cp

@@ -28,6 +28,8 @@ K/V as separate segments, both layouts, against the concatenated call.
 `chunked_kv` times the same share with its K/V arriving in W chunks
 (cp_attn_partial per chunk, then cp_attn_merge).
 
+For the 2D workload the JSON carries `ulysses_2d_fused`: the same step with the
+unpack and the attention replaced by cp_attn_recv_to_send_2d.
 For the workloads without an AllGather-KV stage the JSON also carries
 `ulysses_fused`: the Ulysses-only rank step (attention of the rank's H/W heads
 over the whole sequence, the same FLOPs) timed once with separate unpack and
@@ -457,6 +459,57 @@ def ulysses_chain(path, burst=10):
            "unfused_attn_us": time_burst(attn_unfused, burst) * 1e3,
            "fused_attn_us": time_burst(attn_fused, burst) * 1e3,
            "fused_send_equals_unfused": same}
+    res["step_speedup"] = res["unfused_step_us"] / res["fused_step_us"]
+    return res
+
+
+def ulysses_2d_chain(path, burst=5):
+    """2D-layout rank step (Ulysses x AllGather-KV), unfused and fused, on the step's buffers.
+
+    unfused: pack -> exchange -> unpack (K/V into region 0 of the gathered buffer) ->
+             attention over the gathered K/V -> send layout -> exchange -> merge
+    fused:   pack -> exchange -> cp_attn_recv_to_send_2d (Q and the own region's K/V
+             from the received buffer, the other region from the gathered buffer)
+             -> exchange -> merge
+    Returns step and attention durations (us, graph-replayed bursts) and the largest
+    difference between the two send buffers: the fused call attends the two regions
+    as two key segments, whose tiles start at each region's first key, so its
+    summation order differs from the gathered call's where a region's length is not
+    a multiple of the 64-key tile."""
+    import torch
+    cp, wl = path.cp, path.wl
+    W, B = wl.W, wl.B
+    span = W * wl.S_local
+    k_oth, v_oth = path.k_glob[:, span:], path.v_glob[:, span:]   # contiguous: B == 1
+    snd_f = torch.empty_like(path.snd)
+
+    def attn_fused():
+        cp.cp_attn_recv_to_send_2d(path.recv, k_oth, v_oth, B, W, False, None, None, scale=path.scale, out=snd_f)
+
+    def step_unfused():
+        path.pack()
+        path.exchange_in()
+        path.unpack()
+        path.attn()
+        path.exchange_out(path.send())
+        path.merge()
+
+    def step_fused():
+        path.pack()
+        path.exchange_in()
+        attn_fused()
+        path.exchange_out(snd_f)
+        path.merge()
+
+    step_unfused()
+    step_fused()
+    torch.cuda.synchronize()
+    diff = float((path.send().float() - snd_f.float()).abs().max())
+    res = {"unfused_step_us": time_burst(step_unfused, burst) * 1e3,
+           "fused_step_us": time_burst(step_fused, burst) * 1e3,
+           "unfused_attn_us": time_burst(path.attn, burst) * 1e3,
+           "fused_attn_us": time_burst(attn_fused, burst) * 1e3,
+           "max_abs_diff_fused_vs_unfused": diff}
     res["step_speedup"] = res["unfused_step_us"] / res["fused_step_us"]
     return res
 
@@ -904,6 +957,13 @@ def main():
         c["note"] = ("local-Q/global-KV share with K/V in W chunks: W partial attentions "
                      "(fp32 O + lse) and one merge, against the dense call")
         out["chunked_kv"] = c
+    if args.only is None and path.two_d and not args.no_extras:
+        u = ulysses_2d_chain(path)
+        u["fused_attn_TFLOPs"] = flops / (u["fused_attn_us"] * 1e-6) / 1e12
+        u["fused_step_TFLOPs"] = flops / (u["fused_step_us"] * 1e-6) / 1e12
+        u["note"] = ("2D rank step: the unpack and the gathered-K/V attention against one fused call "
+                     "over the received buffer and the other AllGather rank's resident K/V")
+        out["ulysses_2d_fused"] = u
     if args.only is None and wl.masked and not args.no_extras:
         j = joint_segments(path)
         j["note"] = ("joint attention over image and text K/V segments (text mask only), "

@@ -175,6 +175,7 @@ struct View {
 constexpr int kModeChunked = 1;
 constexpr int kModeTwoSeg = 2;
 constexpr int kModeCross = 4;
+constexpr int kModeSeg1Rows = 8;  // segment 1 has a view (row stride) of its own
 
 // CHUNKED = false: every view of the kernel is plain.  CHUNKED = true: a view may
 // be chunked (each view says whether it is).
@@ -188,10 +189,11 @@ __device__ __forceinline__ long long row_off_t(const View& v, int i) {
 
 struct AttnArgs {
   View qv, kv, ov;  // Q, K and V (one view for both), O
+  View kv1;         // K and V of segment 1
   // Keys come in up to two segments, attended as one sequence in this order:
-  // segment 0 = k, v, mask (Skv keys, tiles [0, nt0)), segment 1 = k1, v1, mask1
-  // (Skv1 keys, dense [B][Skv1][H][D] with K/V's row and head strides, tiles
-  // from nt0 on).  Each segment's last tile may be partial.
+  // segment 0 = k, v, mask through kv (Skv keys, tiles [0, nt0)), segment 1 =
+  // k1, v1, mask1 through kv1 (Skv1 keys, tiles from nt0 on).  Each segment's
+  // last tile may be partial.
   const __bf16* k1;
   const __bf16* v1;
   const uint8_t* mask1;
@@ -232,6 +234,10 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   constexpr bool kTwoSeg = (MODE & kModeTwoSeg) != 0;
   constexpr bool kCross = (MODE & kModeCross) != 0;
   static_assert(!kCross || kChunked, "tiles cross chunks only in chunked views");
+  // Segment 1 with a view of its own (its row stride may differ from segment 0's):
+  // it has lane offsets of its own.  Otherwise both segments share K/V's stride.
+  constexpr bool kSeg1Rows = (MODE & kModeSeg1Rows) != 0;
+  static_assert(!kSeg1Rows || kTwoSeg, "a view of its own for segment 1 needs two segments");
   using C = Cfg<D>;
   // K and V tiles: one array per (operand, key group, buffer).  Separate objects
   // let the compiler see that a fill of one buffer does not alias the reads of
@@ -268,7 +274,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   const __bf16* vbase1 = vbase;
   const uint8_t* mbase1 = nullptr;
   if constexpr (kTwoSeg) {
-    const size_t seg1_off = (size_t(b) * a.Skv1) * a.kv.rs + size_t(h) * a.kv.hs;
+    const size_t seg1_off = size_t(b) * a.kv1.bs + size_t(h) * a.kv1.hs;
     kbase1 = a.k1 + seg1_off;
     vbase1 = a.v1 + seg1_off;
     mbase1 = a.mask1 ? a.mask1 + size_t(b) * a.Skv1 : nullptr;
@@ -322,6 +328,19 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     const int chunk = (slot % C::CHUNKS) ^ C::swz(key);
     goff[j] = uint32_t(key) * rs_bytes + uint32_t(chunk) * 16u - uint32_t(j) * 1024u;
   }
+  const uint32_t rs1_bytes = uint32_t(a.kv1.rs) * 2u;
+  uint32_t goff1[C::SPT];
+#pragma unroll
+  for (int j = 0; j < C::SPT; ++j) {
+    if constexpr (kSeg1Rows) {
+      const int slot = (gw * C::SPT + j) * 64 + lane;
+      const int key = slot / C::CHUNKS;
+      const int chunk = (slot % C::CHUNKS) ^ C::swz(key);
+      goff1[j] = uint32_t(key) * rs1_bytes + uint32_t(chunk) * 16u - uint32_t(j) * 1024u;
+    } else {
+      goff1[j] = 0u;
+    }
+  }
   static_assert(C::SPT == 2 || C::SPT == 4, "fill instructions per wave");
   // off: the lane offset of instruction j (goff[j], or xoff for a tile that
   // spans chunks).
@@ -339,31 +358,33 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // row.  Such a tile takes per-lane offsets row_off(key0 + key) - row_off(key0)
   // (rows past the last key get an offset outside the range and read as zero) and
   // a range up to its last row.
-  auto crosses = [&](int key0, int rows) -> bool {
+  auto crosses = [&](const View& v, int key0, int rows) -> bool {
     if constexpr (!kCross) {
+      (void)v;
       (void)key0;
       (void)rows;
       return false;
     } else {
+      if (kSeg1Rows && !v.chunked) return false;
       uint32_t c, r;
-      a.kv.L.divmod(uint32_t(key0), c, r);
-      return int(r) + rows > int(a.kv.L.d);
+      v.L.divmod(uint32_t(key0), c, r);
+      return int(r) + rows > int(v.L.d);
     }
   };
-  auto xoff = [&](int j, int key0, int rows) -> uint32_t {
+  auto xoff = [&](const View& v, int j, int key0, int rows) -> uint32_t {
     const int slot = (gw * C::SPT + j) * 64 + lane;
     const int key = slot / C::CHUNKS;
     const int chunk = (slot % C::CHUNKS) ^ C::swz(key);
     if (key >= rows) return 0x80000000u;
-    const long long dr = row_off_t<true>(a.kv, key0 + key) - row_off_t<true>(a.kv, key0);
+    const long long dr = row_off_t<true>(v, key0 + key) - row_off_t<true>(v, key0);
     return uint32_t(dr) * 2u + uint32_t(chunk) * 16u - uint32_t(j) * 1024u;
   };
-  auto tile_bytes = [&](int key0, int rows, bool cr) -> int {
+  auto tile_bytes = [&](const View& v, int key0, int rows, bool cr) -> int {
     if (kCross && cr) {
-      const long long last = row_off_t<true>(a.kv, key0 + rows - 1) - row_off_t<true>(a.kv, key0);
+      const long long last = row_off_t<true>(v, key0 + rows - 1) - row_off_t<true>(v, key0);
       return int(uint32_t(last) * 2u + uint32_t(D) * 2u);
     }
-    return int(uint32_t(rows - 1) * rs_bytes + uint32_t(D) * 2u);
+    return int(uint32_t(rows - 1) * (kSeg1Rows ? uint32_t(v.rs) * 2u : rs_bytes) + uint32_t(D) * 2u);
   };
   // The source of tile t (which: 0 = K, 1 = V): its buffer descriptor, and for a
   // tile that spans chunks its first key and row count.  The 64 rows of a tile are
@@ -371,23 +392,26 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   struct FillSrc {
     __amdgpu_buffer_rsrc_t rs;
     int key0, rows;
-    bool cross;
+    bool seg1, cross;
   };
   auto fill_src = [&](int which, int t) -> FillSrc {
     bool s1;
     int key0, len;
     seg_of(t, s1, key0, len);
     const int rows = min(C::BN, len - key0);
-    const bool cr = !s1 && crosses(key0, rows);
-    const __bf16* src = s1 ? (which ? vbase1 : kbase1) + (long long)key0 * a.kv.rs
-                           : (which ? vbase : kbase) + row_off_t<kChunked>(a.kv, key0);
-    return {__builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(src), (short)0, tile_bytes(key0, rows, cr),
+    // (plain two-segment calls share K/V's row stride: segment 1 only changes the base)
+    const View& v = (kSeg1Rows && s1) ? a.kv1 : a.kv;
+    const bool cr = crosses(v, key0, rows);
+    const __bf16* src = (s1 ? (which ? vbase1 : kbase1) : (which ? vbase : kbase)) + row_off_t<kChunked>(v, key0);
+    return {__builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(src), (short)0, tile_bytes(v, key0, rows, cr),
                                               0x00020000),
-            key0, rows, cr};
+            key0, rows, s1, cr};
   };
   // Instruction j of a tile's fill into the tile array dst.
   auto fill_one = [&](const FillSrc& f, int j, char* dst) {
-    fill_j(j, f.rs, dst, (kCross && f.cross) ? xoff(j, f.key0, f.rows) : goff[j]);
+    fill_j(j, f.rs, dst,
+           (kCross && f.cross) ? xoff((kSeg1Rows && f.seg1) ? a.kv1 : a.kv, j, f.key0, f.rows)
+                               : ((kSeg1Rows && f.seg1) ? goff1[j] : goff[j]));
   };
   // A whole tile.
   auto fill = [&](int which, int t, char* dst) {
@@ -1000,7 +1024,7 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
                 size_t ext_o, cp_stream_t stream, float* o_part = nullptr, float* lse = nullptr,
                 const float* st_o = nullptr, const float* st_lse = nullptr,
                 const __bf16* k1 = nullptr, const __bf16* v1 = nullptr, const uint8_t* mask1 = nullptr,
-                int64_t Skv1 = 0) {
+                int64_t Skv1 = 0, const View* kv1 = nullptr) {
   const int64_t bm = 32 * kGroupWaves;
   const int64_t m_tiles = (Sq + bm - 1) / bm;
   const int64_t n_work = B * H * m_tiles;
@@ -1024,6 +1048,14 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
   args.v1 = v1;
   args.mask1 = mask1;
   args.Skv1 = int(Skv1);
+  // segment 1: its own view, else dense [B][Skv1][H][D] with K/V's strides
+  if (kv1) {
+    args.kv1 = *kv1;
+  } else {
+    args.kv1 = kv;
+    args.kv1.bs = (long long)Skv1 * kv.rs;
+    args.kv1.chunked = 0;
+  }
   args.nt0 = int((Skv + 63) / 64);
   const int64_t n_tiles = args.nt0 + (Skv1 + 63) / 64;
   args.n_iter_blk = int((n_tiles + 1) / 2);
@@ -1057,21 +1089,40 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
   // combine: BM * D / 4 threads of 256 per query block
   const dim3 grid{unsigned(n_work * args.nsplit)}, block{unsigned(kThreads)}, cblock{256u},
       cgrid{unsigned(n_work * (D / 8))};
-  const int mode = (kv.chunked || qv.chunked || ov.chunked ? kModeChunked : 0) | (Skv1 > 0 ? kModeTwoSeg : 0) |
-                   (kv.chunked && kv.L.d % 64 != 0 ? kModeCross : 0);
-  if ((mode & kModeTwoSeg) && (mode & kModeChunked)) return CP_ERR_UNSUPPORTED;  // no entry point combines them
+  // The chunked variants address rows through the views at run time (a view that
+  // is not chunked is plain there too).  Segment 1 takes a view of its own when it
+  // is chunked or its row stride differs from segment 0's.
+  const bool seg1 = Skv1 > 0;
+  const bool chunked = kv.chunked || qv.chunked || ov.chunked || (seg1 && args.kv1.chunked);
+  const bool seg1_rows = seg1 && (args.kv1.chunked || kv.chunked || args.kv1.rs != kv.rs);
+  const int mode = (chunked ? kModeChunked : 0) | (seg1 ? kModeTwoSeg : 0) |
+                   ((kv.chunked && kv.L.d % 64 != 0) || (seg1 && args.kv1.chunked && args.kv1.L.d % 64 != 0)
+                        ? kModeCross : 0) |
+                   (seg1_rows ? kModeSeg1Rows : 0);
   auto launch_fwd = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, args); };
   if (D == 128) {
     if (mode == 0) launch_fwd(attn_fwd_kernel<128, 0>);
     else if (mode == kModeChunked) launch_fwd(attn_fwd_kernel<128, kModeChunked>);
     else if (mode == kModeChunked + kModeCross) launch_fwd(attn_fwd_kernel<128, kModeChunked + kModeCross>);
-    else launch_fwd(attn_fwd_kernel<128, kModeTwoSeg>);
+    else if (mode == kModeTwoSeg) launch_fwd(attn_fwd_kernel<128, kModeTwoSeg>);
+    else if (mode == kModeTwoSeg + kModeSeg1Rows) launch_fwd(attn_fwd_kernel<128, kModeTwoSeg + kModeSeg1Rows>);
+    else if (mode == kModeChunked + kModeTwoSeg + kModeSeg1Rows)
+      launch_fwd(attn_fwd_kernel<128, kModeChunked + kModeTwoSeg + kModeSeg1Rows>);
+    else if (mode == kModeChunked + kModeTwoSeg + kModeCross + kModeSeg1Rows)
+      launch_fwd(attn_fwd_kernel<128, kModeChunked + kModeTwoSeg + kModeCross + kModeSeg1Rows>);
+    else return CP_ERR_UNSUPPORTED;
     if (args.nsplit > 1) hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, cblock, 0, s, args);
   } else {
     if (mode == 0) launch_fwd(attn_fwd_kernel<64, 0>);
     else if (mode == kModeChunked) launch_fwd(attn_fwd_kernel<64, kModeChunked>);
     else if (mode == kModeChunked + kModeCross) launch_fwd(attn_fwd_kernel<64, kModeChunked + kModeCross>);
-    else launch_fwd(attn_fwd_kernel<64, kModeTwoSeg>);
+    else if (mode == kModeTwoSeg) launch_fwd(attn_fwd_kernel<64, kModeTwoSeg>);
+    else if (mode == kModeTwoSeg + kModeSeg1Rows) launch_fwd(attn_fwd_kernel<64, kModeTwoSeg + kModeSeg1Rows>);
+    else if (mode == kModeChunked + kModeTwoSeg + kModeSeg1Rows)
+      launch_fwd(attn_fwd_kernel<64, kModeChunked + kModeTwoSeg + kModeSeg1Rows>);
+    else if (mode == kModeChunked + kModeTwoSeg + kModeCross + kModeSeg1Rows)
+      launch_fwd(attn_fwd_kernel<64, kModeChunked + kModeTwoSeg + kModeCross + kModeSeg1Rows>);
+    else return CP_ERR_UNSUPPORTED;
     if (args.nsplit > 1) hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, cblock, 0, s, args);
   }
   return hip_status(hipGetLastError());
@@ -1206,6 +1257,60 @@ extern "C" int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, v
   const __bf16* r = static_cast<const __bf16*>(recv);
   return attn_launch(r, in, r + D, r + 2 * D, in, key_mask, static_cast<__bf16*>(send), out, B, S, S, H_local,
                      D, scale, workspace, workspace_bytes, rb, rb, sb, stream);
+}
+
+extern "C" int cp_attn_recv_to_send_2d(const void* recv, const void* k_other, const void* v_other, int64_t S_other,
+                                       int other_first, const uint8_t* own_mask, const uint8_t* other_mask,
+                                       void* send, int64_t B, int64_t S_local, int64_t H_local, int64_t D,
+                                       int64_t W, float scale, int causal, void* workspace,
+                                       size_t workspace_bytes, cp_stream_t stream) {
+  if (!recv || !send || !k_other || !v_other) return CP_ERR_NULL;
+  if (W < 1 || S_other < 1) return CP_ERR_SHAPE;
+  if (other_first != 0 && other_first != 1) return CP_ERR_UNSUPPORTED;
+  constexpr int64_t kIntMax = 0x7fffffff;
+  if (S_local < 1 || S_local > kIntMax / W) return CP_ERR_SHAPE;
+  const int64_t S = W * S_local;
+  if (S > kIntMax / 2 || S_other > kIntMax / 2) return CP_ERR_SHAPE;
+  if (const int st = attn_check(B, S, S + S_other, H_local, D, scale, causal)) return st;
+  if (!aligned16(recv) || !aligned16(send) || !aligned16(k_other) || !aligned16(v_other)) return CP_ERR_ALIGNMENT;
+  if (workspace && !aligned16(workspace)) return CP_ERR_ALIGNMENT;
+  if (B > kIntMax || S + S_other > kIntMax - 64 || H_local > kIntMax) return CP_ERR_SHAPE;
+  if (H_local * 3 * D * 2 * 64 > kIntMax) return CP_ERR_SHAPE;
+  const int64_t bm = 32 * kGroupWaves;
+  int64_t bh, n_work, re, oe;
+  if (!mul_capped(B, H_local, kIntMax, &bh) || !mul_capped(bh, (S + bm - 1) / bm, kIntMax, &n_work))
+    return CP_ERR_SHAPE;
+  if (!mul_capped(B * S, H_local * 3 * D, int64_t(1) << 60, &re) ||
+      !mul_capped(B * S_other, H_local * D, int64_t(1) << 60, &oe))
+    return CP_ERR_SHAPE;
+  const size_t rb = size_t(re) * 2, sb = size_t(re / 3) * 2, ob = size_t(oe) * 2;
+  // tiles that span the received chunks use 32-bit differences of row offsets
+  if (B > 1 && S_local % 64 != 0 && rb > size_t(kIntMax)) return CP_ERR_SHAPE;
+  if (overlaps(send, sb, recv, rb) || overlaps(send, sb, k_other, ob) || overlaps(send, sb, v_other, ob))
+    return CP_ERR_ALIAS;
+  if (own_mask && overlaps(send, sb, own_mask, size_t(B * S))) return CP_ERR_ALIAS;
+  if (other_mask && overlaps(send, sb, other_mask, size_t(B * S_other))) return CP_ERR_ALIAS;
+  // the workspace must not overlap any operand (checked here over its whole extent)
+  if (workspace && workspace_bytes &&
+      (overlaps(workspace, workspace_bytes, recv, rb) || overlaps(workspace, workspace_bytes, k_other, ob) ||
+       overlaps(workspace, workspace_bytes, v_other, ob) || overlaps(workspace, workspace_bytes, send, sb) ||
+       (own_mask && overlaps(workspace, workspace_bytes, own_mask, size_t(B * S))) ||
+       (other_mask && overlaps(workspace, workspace_bytes, other_mask, size_t(B * S_other)))))
+    return CP_ERR_ALIAS;
+  const View in = chunked_view(B, S_local, H_local, 3 * D, H_local * 3 * D);
+  const View out = chunked_view(B, S_local, H_local, D, H_local * D);
+  const View oth = plain_view(S_other, H_local, D);
+  const __bf16* r = static_cast<const __bf16*>(recv);
+  const auto* ko = static_cast<const __bf16*>(k_other);
+  const auto* vo = static_cast<const __bf16*>(v_other);
+  auto* sp = static_cast<__bf16*>(send);
+  if (other_first)
+    return attn_launch(r, in, ko, vo, oth, other_mask, sp, out, B, S, S_other, H_local, D, scale, workspace,
+                       workspace_bytes, rb, ob, sb, stream, nullptr, nullptr, nullptr, nullptr, r + D, r + 2 * D,
+                       own_mask, S, &in);
+  return attn_launch(r, in, r + D, r + 2 * D, in, own_mask, sp, out, B, S, S, H_local, D, scale, workspace,
+                     workspace_bytes, rb, rb, sb, stream, nullptr, nullptr, nullptr, nullptr, ko, vo, other_mask,
+                     S_other, &oth);
 }
 
 namespace {

@@ -385,6 +385,63 @@ def cp_attn_recv_to_send(recv, B: int, W: int, key_mask=None, scale=None, out=No
     return out
 
 
+def cp_attn_recv_to_send_2d(recv, k_other, v_other, B: int, W: int, other_first: bool = False,
+                            own_mask=None, other_mask=None, scale=None, out=None, causal=False,
+                            stream=None, split=True, workspace=None) -> torch.Tensor:
+    """2D-layout Ulysses attention from the received staging buffer into the send layout.
+
+    recv [W, B*S_l, H_l, 3D] bf16 (this rank's Ulysses group) and the other
+    AllGather rank's head-sharded k_other / v_other [B, S_other, H_l, D] ->
+    send [W, B, S_l, H_l, D]: the attention of the H_l heads of the rank's
+    W*S_l rows over both key ranges (the other rank's first when other_first),
+    equal bit for bit to unpack -> cp_attn_joint -> cp_output_reverse(0).
+    own_mask: uint8/bool [B, W*S_l] or None; other_mask: [B, S_other] or None.
+    split / workspace as for cp_attn_localq_globalkv.
+    """
+    lib = _lib.load()
+    W_, rows, Hl, D3 = recv.shape
+    if W_ != W or rows % B or D3 % 3:
+        raise ValueError("recv shape does not match W / B")
+    if recv.dtype != torch.bfloat16 or k_other.dtype != torch.bfloat16 or v_other.dtype != torch.bfloat16:
+        raise TypeError("attention takes bfloat16")
+    Sl, D = rows // B, D3 // 3
+    S = W * Sl
+    if k_other.dim() != 4 or k_other.shape[0] != B or k_other.shape[2] != Hl or k_other.shape[3] != D:
+        raise ValueError("k_other must be [B, S_other, H_l, D]")
+    if tuple(v_other.shape) != tuple(k_other.shape):
+        raise ValueError("v_other must have k_other's shape")
+    So = k_other.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+
+    def mask_arg(m, n, name):
+        if m is None:
+            return None
+        if m.dtype not in (torch.uint8, torch.bool) or tuple(m.shape) != (B, n):
+            raise ValueError(f"{name} must be uint8/bool [B, {n}]")
+        return _dev(m, name)
+
+    om, xm = mask_arg(own_mask, S, "own_mask"), mask_arg(other_mask, So, "other_mask")
+    shape = (W, B, Sl, Hl, D)
+    if out is None:
+        out = torch.empty(shape, dtype=recv.dtype, device=recv.device)
+    if tuple(out.shape) != shape or out.dtype != recv.dtype:
+        raise ValueError(f"out must be {shape} {recv.dtype}")
+    ws_ptr, ws_bytes = None, 0
+    if split:
+        need = int(lib.cp_attn_workspace_bytes(B, S, S + So, Hl, D))
+        if workspace is None:
+            workspace = staging_buffer("attn_workspace", (max(need, 16),), torch.uint8, recv.device)
+        elif workspace.dtype != torch.uint8 or workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor")
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel()
+    _lib.check("cp_attn_recv_to_send_2d", lib.cp_attn_recv_to_send_2d(
+        _dev(recv, "recv"), _dev(k_other, "k_other"), _dev(v_other, "v_other"), So, int(bool(other_first)),
+        om, xm, _dev(out, "send"), B, Sl, Hl, D, W, float(scale), int(bool(causal)), ws_ptr, ws_bytes,
+        _stream(stream)))
+    return out
+
+
 def cp_attn_workspace_bytes(B: int, Sq: int, Skv: int, H: int, D: int) -> int:
     """Workspace bytes cp_attn_localq_globalkv may use with split=True (upper bound, current device)."""
     return int(_lib.load().cp_attn_workspace_bytes(B, Sq, Skv, H, D))

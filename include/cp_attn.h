@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CP_ABI_VERSION 7
+#define CP_ABI_VERSION 8
 
 typedef struct ihipStream_t* cp_stream_t; /* == hipStream_t */
 
@@ -343,6 +343,40 @@ int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, void* send,
                          int64_t B, int64_t S_local, int64_t H_local, int64_t D, int64_t W,
                          float scale, int causal, void* workspace, size_t workspace_bytes,
                          cp_stream_t stream);
+
+/*
+ * The same for the 2D layout ([vllm-omni#7641]: Ulysses groups of W ranks inside
+ * AllGather-KV groups): the rank's keys are its own Ulysses group's sequence,
+ * received in recv, and the sequence of the other AllGather rank, whose
+ * head-sharded K and V (the same heads) are already resident.  The two key
+ * ranges are attended as one sequence, the other rank's first when other_first
+ * is 1 (it holds the earlier sequence region), else after the rank's own.  The
+ * result equals
+ *
+ *   cp_unpack_head_sharded(recv) -> cp_attn_joint(q, own K/V, other K/V, in the
+ *   order above) with Sq = W*S_local, H = H_local -> cp_output_reverse(SEND)
+ *
+ * bit for bit, without the intermediate Q/K/V and O buffers.
+ *
+ *   recv       : [W][B*S_local][H_local][3*D] bf16 (q, k, v concatenated per head)
+ *   k_other,
+ *   v_other    : [B][S_other][H_local][D] bf16
+ *   own_mask   : NULL, or [B][W*S_local] uint8 over the rank's own keys
+ *   other_mask : NULL, or [B][S_other] uint8 over the other rank's keys
+ *   send       : [W][B][S_local][H_local][D] bf16
+ *   workspace  : as for cp_attn_localq_globalkv_ws (sized by
+ *                cp_attn_workspace_bytes(B, W*S_local, W*S_local + S_other, H_local, D)),
+ *                or NULL; it must not overlap any operand
+ *
+ * Requires what cp_attn_recv_to_send requires, S_other >= 1, other_first in
+ * {0, 1} (CP_ERR_UNSUPPORTED otherwise), k_other / v_other 16-byte aligned and
+ * disjoint from send.
+ */
+int cp_attn_recv_to_send_2d(const void* recv, const void* k_other, const void* v_other, int64_t S_other,
+                            int other_first, const uint8_t* own_mask, const uint8_t* other_mask,
+                            void* send, int64_t B, int64_t S_local, int64_t H_local, int64_t D,
+                            int64_t W, float scale, int causal, void* workspace, size_t workspace_bytes,
+                            cp_stream_t stream);
 
 /*
  * Ulysses output exchange ([sglang#33667] names _usp_output_all_to_all in its

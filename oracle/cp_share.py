@@ -100,6 +100,68 @@ def ulysses_attention_send(recv, B, W, key_mask=None, scale=None):
     return _layout.output_reverse_send(o, W)
 
 
+def ulysses_2d_attention_send(recv, k_other, v_other, B, W, other_first=False, own_mask=None,
+                              other_mask=None, scale=None):
+    """One rank of the 2D layout with A = 2 between its Ulysses exchanges: the
+    received ``[W, B*S_l, H_l, 3D]`` buffer of its own Ulysses group and the other
+    AllGather rank's head-sharded ``k_other`` / ``v_other`` ``[B, S_o, H_l, D]`` ->
+    send layout ``[W, B, S_l, H_l, D]`` of the attention of the rank's rows over
+    both key ranges in sequence order (the other rank's region first when it holds
+    the earlier one).  Masks: ``[B, W*S_l]`` over the own keys, ``[B, S_o]`` over
+    the other rank's, None = attend."""
+    q, k, v = _layout.unpack_head_sharded(recv, B, W)
+    S, So = k.shape[1], k_other.shape[1]
+    own = (k, v, own_mask, S)
+    oth = (k_other, v_other, other_mask, So)
+    first, second = (oth, own) if other_first else (own, oth)
+    kk = np.concatenate([first[0], second[0]], axis=1)
+    vv = np.concatenate([first[1], second[1]], axis=1)
+    mask = None
+    if own_mask is not None or other_mask is not None:
+        parts = [np.ones((B, n), dtype=np.uint8) if m is None else np.asarray(m, dtype=np.uint8)
+                 for (_, _, m, n) in (first, second)]
+        mask = np.concatenate(parts, axis=1)
+    o = _attn.attention(q, kk, vv, key_mask=mask, scale=scale)
+    return _layout.output_reverse_send(o, W)
+
+
+def composed_2d_fused(q_full, k_full, v_full, U, key_mask=None, scale=None):
+    """The 2D layout with A = 2, every rank through ``ulysses_2d_attention_send``.
+
+    Rank (a, u) receives its Ulysses group's exchange (region a, head slice u); the
+    other AllGather rank of its group u is (1 - a, u), whose unpacked K/V (region
+    1 - a, the same heads) it attends as well, region 0 first.  Returns
+    ``(fused_inputs, outputs)``: ``fused_inputs[g] = (recv, k_other, v_other,
+    other_first, own_mask, other_mask)`` and rank g's final ``[B, S_l, H, D]``."""
+    A = 2
+    B, S, H, D = q_full.shape
+    P = U * A
+    if S % P or H % U:
+        raise ValueError("S must divide by 2U and H by U")
+    Sl, Sr = S // P, S // A
+    shard = [tuple(t[:, g * Sl:(g + 1) * Sl] for t in (q_full, k_full, v_full)) for g in range(P)]
+    recv = [None] * P
+    for group in ulysses_groups(U, A):
+        r = _layout.exchange([_layout.pack_qkv_dst_major(*shard[g], U) for g in group])
+        for u, g in enumerate(group):
+            recv[g] = r[u]
+    inputs, snd = [None] * P, [None] * P
+    for a in range(A):
+        for u in range(U):
+            g, go = a * U + u, (1 - a) * U + u
+            _, k_o, v_o = _layout.unpack_head_sharded(recv[go], B, U)
+            own_m = None if key_mask is None else key_mask[:, a * Sr:(a + 1) * Sr]
+            oth_m = None if key_mask is None else key_mask[:, (1 - a) * Sr:(2 - a) * Sr]
+            inputs[g] = (recv[g], k_o, v_o, a == 1, own_m, oth_m)
+            snd[g] = ulysses_2d_attention_send(recv[g], k_o, v_o, B, U, a == 1, own_m, oth_m, scale)
+    outputs = [None] * P
+    for group in ulysses_groups(U, A):
+        rcv = _layout.exchange([snd[g] for g in group])
+        for u, g in enumerate(group):
+            outputs[g] = _layout.output_reverse_merge(rcv[u])
+    return inputs, outputs
+
+
 def ulysses_attention_all(q_full, k_full, v_full, W, key_mask=None, scale=None):
     """Every rank of one Ulysses group: pack, exchange, ``ulysses_attention_send``,
     exchange, merge.  Returns ``(recv, outputs)``: each rank's received staging

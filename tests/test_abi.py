@@ -120,6 +120,15 @@ def _fused(**kw):
                                             a["W"], a["scale"], a["causal"], a["ws"], a["nbytes"], None)
 
 
+def _fused2d(**kw):
+    a = dict(r=A, ko=A + 2 * BIG, vo=A + 3 * BIG, So=256, first=0, om=None, xm=None, s=A + BIG, B=1, Sl=128,
+             Hl=2, D=128, W=2, scale=0.125, causal=0, ws=None, nbytes=0)
+    a.update(kw)
+    return _lib.load().cp_attn_recv_to_send_2d(a["r"], a["ko"], a["vo"], a["So"], a["first"], a["om"], a["xm"],
+                                               a["s"], a["B"], a["Sl"], a["Hl"], a["D"], a["W"], a["scale"],
+                                               a["causal"], a["ws"], a["nbytes"], None)
+
+
 def _partial(**kw):
     a = dict(q=A, k=A + BIG, v=A + 2 * BIG, m=None, o=A + 3 * BIG, lse=A + 4 * BIG, B=1, Sq=8, Skv=16,
              H=2, D=128, scale=0.125, causal=0)
@@ -257,6 +266,31 @@ def test_attention_ws_rejects(kw, code):
 ])
 def test_recv_to_send_rejects(kw, code):
     assert _fused(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(r=None), _lib.CP_ERR_NULL),
+    (dict(ko=None), _lib.CP_ERR_NULL),
+    (dict(vo=None), _lib.CP_ERR_NULL),
+    (dict(s=None), _lib.CP_ERR_NULL),
+    (dict(So=0), _lib.CP_ERR_SHAPE),
+    (dict(W=0), _lib.CP_ERR_SHAPE),
+    (dict(Sl=0), _lib.CP_ERR_SHAPE),
+    (dict(first=2), _lib.CP_ERR_UNSUPPORTED),
+    (dict(D=96), _lib.CP_ERR_HEAD_DIM),
+    (dict(scale=0.0), _lib.CP_ERR_SCALE),
+    (dict(causal=1), _lib.CP_ERR_UNSUPPORTED),
+    (dict(ko=A + 2 * BIG + 8), _lib.CP_ERR_ALIGNMENT),
+    (dict(s=A + 4096), _lib.CP_ERR_ALIAS),                      # send overlaps recv
+    (dict(s=A + 2 * BIG + 64), _lib.CP_ERR_ALIAS),              # send overlaps k_other
+    (dict(xm=A + BIG + 64), _lib.CP_ERR_ALIAS),                 # other mask inside send
+    (dict(ws=A + 3 * BIG, nbytes=1 << 20), _lib.CP_ERR_ALIAS),  # workspace overlaps v_other
+    (dict(B=2, Sl=70, Hl=10000), _lib.CP_ERR_SHAPE),           # tiles span chunks, recv over 2 GB
+    (dict(Sl=1 << 30, W=4), _lib.CP_ERR_SHAPE),
+])
+def test_recv_to_send_2d_rejects(kw, code):
+    assert _fused2d(**kw) == code
 
 
 @cpu_only

@@ -255,6 +255,43 @@ def test_recv_to_send_matches_oracle_and_unfused(gu, B, W, Sl, Hl, D, masked):
     _assert_close(gu.to_f64(got), ref, f"recv_to_send B{B} W{W} Sl{Sl} Hl{Hl} D{D}")
 
 
+@pytest.mark.parametrize("B,W,Sl,Hl,D,So,other_first,masked", [
+    (1, 2, 128, 2, 64, 256, False, False),   # region 0 of a U=2 x A=2 layout
+    (1, 2, 128, 2, 64, 256, True, False),    # region 1: the other rank's keys first
+    (1, 2, 70, 2, 128, 140, True, True),     # ragged: segments end mid-tile, row strides 3D*H vs D*H
+    (2, 2, 64, 3, 128, 128, False, True),    # several batches: chunked received rows
+    (2, 3, 70, 1, 64, 210, True, True),      # chunked rows whose tiles span chunks, two segments
+    (1, 4, 512, 1, 128, 2048, False, False), # split-KV
+])
+def test_recv_to_send_2d_matches_oracle_and_unfused(gu, B, W, Sl, Hl, D, So, other_first, masked):
+    import context_attention_diffusion_amd as cp
+    from oracle import cp_share
+    seed = 7500 + B * 100 + W * 10 + Sl + D + So + int(other_first)
+    recv = _rand_bits((W, B * Sl, Hl, 3 * D), seed)
+    ko, vo = _rand_bits((B, So, Hl, D), seed + 1), _rand_bits((B, So, Hl, D), seed + 2)
+    S = W * Sl
+    om = xm = None
+    if masked:
+        rng = np.random.default_rng(seed + 3)
+        om = (rng.random((B, S)) > 0.3).astype(np.uint8)
+        xm = (rng.random((B, So)) > 0.3).astype(np.uint8)
+        om[:, -1] = 1
+    rd, kd, vd = gu.to_dev(recv), gu.to_dev(ko), gu.to_dev(vo)
+    omd = None if om is None else torch.from_numpy(om).to(gu.DEV)
+    xmd = None if xm is None else torch.from_numpy(xm).to(gu.DEV)
+    print(f"[attn] recv_to_send_2d B={B} W={W} Sl={Sl} Hl={Hl} D={D} So={So} other_first={other_first} "
+          f"masked={masked}", flush=True)
+    got = cp.cp_attn_recv_to_send_2d(rd, kd, vd, B, W, other_first, omd, xmd)
+    q, k, v = cp.cp_unpack_head_sharded(rd, B, W)
+    o = cp.cp_attn_joint(q, k, v, kd, vd, omd, xmd, joint_front=other_first)
+    ref_gpu = cp.cp_output_reverse(0, o, W, B)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref_gpu), "fused result differs from unpack -> joint attention -> send"
+    ref = cp_share.ulysses_2d_attention_send(bf16.bits_to_f64(recv), bf16.bits_to_f64(ko), bf16.bits_to_f64(vo),
+                                             B, W, other_first, om, xm)
+    _assert_close(gu.to_f64(got), ref, f"recv_to_send_2d B{B} W{W} Sl{Sl} Hl{Hl} D{D} So{So}")
+
+
 @pytest.mark.parametrize("name", ["image_cp4", "joint_cfg_cp4"])
 def test_recv_to_send_full_size_sampled(gu, name):
     """Rank 0 of the workload's Ulysses group at full size: sampled rows against the

@@ -227,6 +227,42 @@ def test_ulysses_attention_ranks_reassemble_full_attention(W, masked):
                                        rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("U", [2, 3])
+@pytest.mark.parametrize("masked", [False, True])
+def test_fused_2d_ranks_reassemble_full_attention(U, masked):
+    # 2D layout, A = 2: each rank attends its Ulysses group's received rows over its
+    # own region plus the other AllGather rank's region (region 0 first); after the
+    # reverse exchange the ranks' outputs, in global rank order, are full attention,
+    # the same as the gathered-K/V composition.
+    B, S, H, D = 2, 24 * U, 2 * U, 4
+    q, k, v = _rand((B, S, H, D), 54), _rand((B, S, H, D), 55), _rand((B, S, H, D), 56)
+    m = _mask(B, S, 57) if masked else None
+    ins, outs = cp_share.composed_2d_fused(q, k, v, U, m)
+    full = A.attention(q, k, v, m)
+    np.testing.assert_allclose(np.concatenate(outs, axis=1), full, rtol=1e-12, atol=1e-13)
+    _, outs_g = cp_share.composed_2d(q, k, v, U, 2, m)
+    for a, b in zip(outs, outs_g):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+    # the rank of region 1 takes the other region first; a rank of region 0 after
+    assert [x[3] for x in ins] == [False] * U + [True] * U
+
+
+def test_fused_2d_order_and_masks_enter_as_segments():
+    # Swapping which range comes first changes nothing but the order of the keys
+    # (attention is invariant under key permutation), and a mask part of zeros
+    # removes that range: then the result is the own range's attention alone.
+    B, W, Sl, Hl, D, So = 1, 2, 6, 2, 4, 9
+    rng = np.random.default_rng(58)
+    recv = rng.standard_normal((W, B * Sl, Hl, 3 * D))
+    ko, vo = rng.standard_normal((B, So, Hl, D)), rng.standard_normal((B, So, Hl, D))
+    a0 = cp_share.ulysses_2d_attention_send(recv, ko, vo, B, W, False)
+    a1 = cp_share.ulysses_2d_attention_send(recv, ko, vo, B, W, True)
+    np.testing.assert_allclose(a0, a1, rtol=1e-12, atol=1e-13)
+    none = np.zeros((B, So), dtype=np.uint8)
+    got = cp_share.ulysses_2d_attention_send(recv, ko, vo, B, W, True, None, none)
+    np.testing.assert_allclose(got, cp_share.ulysses_attention_send(recv, B, W), rtol=1e-12, atol=1e-13)
+
+
 @pytest.mark.parametrize("masked", [False, True])
 @pytest.mark.parametrize("cuts", [(7,), (1, 20), (5, 6, 30)])
 def test_chunked_keys_merge_to_full_attention(masked, cuts):

@@ -13,6 +13,8 @@ Plain numpy, float64 for floating point, bf16 carried as uint16 bit patterns:
 * ``oracle.attention`` -- softmax(scale * Q K^T) V with an optional key-validity mask;
 * ``oracle.cp_share``  -- the AllGather-KV and 2D (Ulysses x AllGather-KV) rank layouts
                           composed from the above, for end-to-end invariants.
+* ``oracle.varlen``    -- packed variable-length attention: the per-rank remap of the
+                          packed query boundaries and per-document attention.
 
 Sources, cited by page title and section:
 

@@ -33,17 +33,24 @@ from . import attention as _attn
 
 def remap_cu_seqlens_q(cu_q_global, rank, S_local):
     """Local query boundaries of AllGather-KV rank ``rank`` whose span is
-    ``[rank*S_local, (rank+1)*S_local)``: document i becomes
-    ``[max(lo_i, s0), min(hi_i, s1))`` shifted by ``-s0``, empty when the two do not
-    meet (its start and end then coincide)."""
+    ``[s0, s1) = [rank*S_local, (rank+1)*S_local)``.  Document i, global rows
+    ``[lo_i, hi_i)``, keeps the local rows ``[max(lo_i, s0), min(hi_i, s1)) - s0``,
+    an empty range placed at the clamped position when the two do not meet, so
+    every document keeps one entry and document i's local rows are exactly its
+    rows inside the span."""
     cu = [int(x) for x in cu_q_global]
     s0, s1 = rank * S_local, (rank + 1) * S_local
-    local = [0]
+    starts, ends = [], []
     for i in range(len(cu) - 1):
-        lo, hi = max(cu[i], s0), min(cu[i + 1], s1)
-        n = max(0, hi - lo)
-        local.append(local[-1] + n)
-    return np.asarray(local, dtype=np.int64)
+        lo, hi = cu[i], cu[i + 1]
+        a = min(max(lo, s0), s1)          # intersection [a, b) of [lo, hi) with [s0, s1)
+        b = max(min(hi, s1), a)
+        starts.append(a - s0)
+        ends.append(b - s0)
+    # consecutive documents share a boundary: document i ends where i + 1 starts
+    for i in range(len(starts) - 1):
+        assert ends[i] == starts[i + 1]
+    return np.asarray(starts + ends[-1:], dtype=np.int64)
 
 
 def _check_cu(cu, total, name):

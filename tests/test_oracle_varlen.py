@@ -56,11 +56,12 @@ def test_remap_invariants(seed):
     S = A * Sl
     n = int(rng.integers(1, 7))
     cu = np.sort(rng.integers(0, S + 1, size=n + 1))
-    cu[0] = 0
+    if seed % 2 == 0:
+        cu[0] = 0                       # the usual packing; odd seeds leave rows before document 0
     lens = np.zeros(n, dtype=np.int64)
     for r in range(A):
         loc = V.remap_cu_seqlens_q(cu, r, Sl)
-        assert loc.size == n + 1 and loc[0] == 0 and (np.diff(loc) >= 0).all() and loc[-1] <= Sl
+        assert loc.size == n + 1 and loc[0] >= 0 and (np.diff(loc) >= 0).all() and loc[-1] <= Sl
         # local row j of document i is global row r*Sl + j, and lies inside document i
         for i in range(n):
             for j in range(loc[i], loc[i + 1]):

@@ -28,6 +28,10 @@ K/V as separate segments, both layouts, against the concatenated call.
 `chunked_kv` times the same share with its K/V arriving in W chunks
 (cp_attn_partial per chunk, then cp_attn_merge).
 
+`packed_varlen` (unmasked B = 1 AllGather-KV workloads) packs the sequence as
+four documents and times, for every AllGather-KV rank, the remap of the packed
+query boundaries plus cp_attn_varlen over the rank's rows.
+
 For the 2D workload the JSON carries `ulysses_2d_fused`: the same step with the
 unpack and the attention replaced by cp_attn_recv_to_send_2d.
 For the workloads without an AllGather-KV stage the JSON also carries
@@ -593,6 +597,37 @@ def joint_segments(path, burst=10):
     return res
 
 
+def packed_varlen(path, n_docs=4, burst=10):
+    """The AllGather-KV share with its sequence packed as n_docs documents (seeded cut
+    points): for every AllGather-KV rank, the device-side remap of the global query
+    boundaries to the rank's rows and the packed attention of its local rows over
+    the global keys, each document attending to itself only."""
+    import torch
+    import workloads
+    cp, wl = path.cp, path.wl
+    Sl = wl.attn_rows
+    A = wl.S // Sl
+    cu = workloads.packed_boundaries(wl, n_docs)
+    g = torch.tensor(cu, dtype=torch.int32, device=path.attn_q.device)
+    q, k, v = path.attn_q[0], path.attn_k[0], path.attn_v[0]
+    loc = torch.empty_like(g)
+    out = torch.zeros_like(q)
+    H, D = q.shape[1], q.shape[2]
+    ranks = []
+    for r in range(A):
+        def call(r=r):
+            cp.cp_varlen_remap_cu_seqlens_q(g, r, Sl, out=loc)
+            cp.cp_attn_varlen(q, k, v, loc, g, scale=path.scale, out=out)
+        call()
+        torch.cuda.synchronize()
+        lq = loc.cpu().tolist()
+        flops = sum(4 * H * D * (lq[i + 1] - lq[i]) * (cu[i + 1] - cu[i]) for i in range(n_docs))
+        us = time_burst(call, burst) * 1e3
+        ranks.append({"rank": r, "local_cu_seqlens_q": lq, "us": us, "flops": flops,
+                      "TFLOPs": flops / (us * 1e-6) / 1e12})
+    return {"cu_seqlens": cu, "ranks": ranks}
+
+
 def uaa_compare(seqs, heads=14, D=128, seed=1240):
     """Per-rank comparison of a padded Ulysses layout against the composed one, at the
     shapes of the pages' attention benchmark (heads 14, D 128, four ranks):
@@ -964,6 +999,12 @@ def main():
         u["note"] = ("2D rank step: the unpack and the gathered-K/V attention against one fused call "
                      "over the received buffer and the other AllGather rank's resident K/V")
         out["ulysses_2d_fused"] = u
+    if args.only is None and not path.two_d and not wl.masked and wl.B == 1 and not args.no_extras:
+        p = packed_varlen(path)
+        p["dense_us"] = kern["attn"]["us"] if "attn" in kern else None
+        p["note"] = ("AllGather-KV share with the sequence packed as 4 documents: per rank, the remap of "
+                     "the packed query boundaries and the packed attention (both timed)")
+        out["packed_varlen"] = p
     if args.only is None and wl.masked and not args.no_extras:
         j = joint_segments(path)
         j["note"] = ("joint attention over image and text K/V segments (text mask only), "

@@ -46,6 +46,9 @@ SIGNATURES = {
     "cp_attn_merge": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]),
     "cp_attn_recv_to_send": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                             ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t, _vp]),
+    "cp_varlen_remap_cu_seqlens_q": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp]),
+    "cp_attn_varlen": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64,
+                                      ctypes.c_float, ctypes.c_int, _vp]),
     "cp_attn_recv_to_send_2d": (ctypes.c_int, [_vp, _vp, _vp, _i64, ctypes.c_int, _vp, _vp, _vp, _i64, _i64,
                                                _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, _vp,
                                                ctypes.c_size_t, _vp]),
@@ -67,7 +70,7 @@ CP_ERR_WORKSPACE = 11
 
 CP_DTYPE_BF16 = 0
 CP_DTYPE_FP16 = 1
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 _lib = None
 

@@ -176,6 +176,7 @@ constexpr int kModeChunked = 1;
 constexpr int kModeTwoSeg = 2;
 constexpr int kModeCross = 4;
 constexpr int kModeSeg1Rows = 8;  // segment 1 has a view (row stride) of its own
+constexpr int kModeVarlen = 16;   // packed documents: batch index b is document b
 
 // CHUNKED = false: every view of the kernel is plain.  CHUNKED = true: a view may
 // be chunked (each view says whether it is).
@@ -223,6 +224,13 @@ struct AttnArgs {
   // o_part / lse), folded into this call's result; NULL: none.
   const float* st_o;
   const float* st_lse;
+  // Packed documents (varlen variant only): document b takes query rows
+  // [cu_q[b], cu_q[b+1]) of the Sq packed rows and key rows [cu_k[b], cu_k[b+1])
+  // of the Skv packed keys; B is the document count.  A query block is a BM-row
+  // tile of the packed rows (m_tiles = ceil(Sq / BM) per head) and runs every
+  // document that has rows in it, one after the other.
+  const int* cu_q;
+  const int* cu_k;
 };
 
 // The body is a device function behind a thin kernel: the LDS address-space
@@ -238,6 +246,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // it has lane offsets of its own.  Otherwise both segments share K/V's stride.
   constexpr bool kSeg1Rows = (MODE & kModeSeg1Rows) != 0;
   static_assert(!kSeg1Rows || kTwoSeg, "a view of its own for segment 1 needs two segments");
+  constexpr bool kVarlen = (MODE & kModeVarlen) != 0;
+  static_assert(!kVarlen || MODE == kModeVarlen, "packed documents use plain views and one key segment");
   using C = Cfg<D>;
   // K and V tiles: one array per (operand, key group, buffer).  Separate objects
   // let the compiler see that a fill of one buffer does not alias the reads of
@@ -262,13 +272,43 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // One segment: query block `work`, iterations [i0, i1) of it.  slot_idx < 0:
   // the segment is the whole block and writes O; otherwise it writes its
   // partial state to workspace slot slot_idx.
-  auto process = [&](int work, int i0, int i1, int slot_idx) {
-  const int mt = work % a.m_tiles;
+  // vdoc: the document a packed-documents block runs (varlen variant only).
+  auto process = [&](int work, int i0, int i1, int slot_idx, int vdoc) {
+  // Packed documents: query block = (head, BM-row tile of the packed rows), numbered
+  // head-major so that one head's blocks stay on one XCD.
+  const int mt = kVarlen ? 0 : work % a.m_tiles;
   const int bh = work / a.m_tiles;
-  const int h = bh % a.H;
-  const int b = bh / a.H;
-  const __bf16* kbase = a.k + b * a.kv.bs + h * a.kv.hs;
-  const __bf16* vbase = a.v + b * a.kv.bs + h * a.kv.hs;
+  const int h = kVarlen ? bh : bh % a.H;
+  const int b = kVarlen ? vdoc : bh / a.H;
+  // Query rows [q_lo, Sq) of the block (relative to q_boff) and keys of its batch row.
+  int q_lo = 0, Sq = a.Sq, Skv = a.Skv;
+  long long q_boff = (long long)b * a.qv.bs, kv_boff = (long long)b * a.kv.bs, o_boff = (long long)b * a.ov.bs;
+  if constexpr (kVarlen) {
+    // The boundaries are read from device memory: clamp them into the packed
+    // buffers so that malformed ones cannot address outside them.
+    const int r0 = (work % a.m_tiles) * C::BM;  // packed row of the tile's first row
+    const int q0 = min(max(a.cu_q[b], 0), a.Sq), q1 = min(max(a.cu_q[b + 1], q0), a.Sq);
+    const int k0 = min(max(a.cu_k[b], 0), a.Skv), k1 = min(max(a.cu_k[b + 1], k0), a.Skv);
+    q_lo = __builtin_amdgcn_readfirstlane(q0 - r0);
+    Sq = __builtin_amdgcn_readfirstlane(q1 - r0);
+    Skv = __builtin_amdgcn_readfirstlane(k1 - k0);
+    q_boff = (long long)r0 * a.qv.rs;
+    o_boff = (long long)r0 * a.ov.rs;
+    kv_boff = (long long)__builtin_amdgcn_readfirstlane(k0) * a.kv.rs;
+    if (Skv == 0) {
+      // no key: the document's rows in this tile are zero
+      constexpr int kVec = D / 8;
+      for (int e = tid; e < C::BM * kVec; e += kThreads) {
+        const int row = e / kVec;
+        if (row >= q_lo && row < Sq)
+          *reinterpret_cast<uint4*>(a.o + o_boff + (long long)row * a.ov.rs + h * a.ov.hs + (e % kVec) * 8) =
+              make_uint4(0u, 0u, 0u, 0u);
+      }
+      return;
+    }
+  }
+  const __bf16* kbase = a.k + kv_boff + h * a.kv.hs;
+  const __bf16* vbase = a.v + kv_boff + h * a.kv.hs;
   const uint8_t* mbase = a.mask ? a.mask + size_t(b) * a.Skv : nullptr;
   const __bf16* kbase1 = kbase;  // segment 1 (two-segment variant only)
   const __bf16* vbase1 = vbase;
@@ -288,7 +328,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     } else {
       s1 = false;
       key0 = t * C::BN;
-      len = a.Skv;
+      len = Skv;
     }
   };
 
@@ -296,8 +336,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   const int q_row = mt * C::BM + gw * 32 + l32;
   bf16x8 qf[C::KS];
   {
-    const bool ok = q_row < a.Sq;
-    const __bf16* qp = a.q + b * a.qv.bs + row_off_t<kChunked>(a.qv, ok ? q_row : 0) + h * a.qv.hs;
+    const bool ok = q_row < Sq && q_row >= q_lo;
+    const __bf16* qp = a.q + q_boff + row_off_t<kChunked>(a.qv, ok ? q_row : 0) + h * a.qv.hs;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       bf16x8 t = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + 8 * hi);
@@ -306,8 +346,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     }
   }
 
-  const int n_tiles = kTwoSeg ? a.nt0 + (a.Skv1 + C::BN - 1) / C::BN : (a.Skv + C::BN - 1) / C::BN;
-  const int n_iter = i1 - i0;  // iterations of every wave in this segment
+  const int n_tiles = kTwoSeg ? a.nt0 + (a.Skv1 + C::BN - 1) / C::BN : (Skv + C::BN - 1) / C::BN;
+  // iterations of every wave in this segment (a document: all of its key tiles)
+  const int n_iter = kVarlen ? (n_tiles + 1) / 2 : i1 - i0;
   // tiles of key group g in the segment: global tiles 2 (i0 + j) + g < n_tiles
   auto tiles_of_group = [&](int g) { return min(n_iter, max(0, (n_tiles - g + 1) / 2 - i0)); };
   const int n_g = tiles_of_group(grp);
@@ -853,7 +894,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     // dword pair hands lane l the run of g = 2k and lane l + 32 that of g = 2k + 1,
     // so each lane stores 16 contiguous bytes.  (Both lanes of a pair hold the same
     // query row, so they are valid or not together.)
-    __bf16* op = a.o + b * a.ov.bs + row_off_t<kChunked>(a.ov, q_row < a.Sq ? q_row : 0) + h * a.ov.hs;
+    const bool o_ok = q_row < Sq && q_row >= q_lo;
+    __bf16* op = a.o + o_boff + row_off_t<kChunked>(a.ov, o_ok ? q_row : 0) + h * a.ov.hs;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -868,7 +910,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
         const auto s0 = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
         const auto s1 = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
         const uint4 out = make_uint4(s0[0], s1[0], s0[1], s1[1]);
-        if (q_row < a.Sq) *reinterpret_cast<uint4*>(op + db * 32 + 8 * (2 * k + hi)) = out;
+        if (o_ok) *reinterpret_cast<uint4*>(op + db * 32 + 8 * (2 * k + hi)) = out;
       }
   }
   };  // process
@@ -876,16 +918,47 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   const int n_iter_blk = a.n_iter_blk;
   // XCD-aware numbering: consecutive logical indices (query blocks, or the
   // parts of one block) run on one XCD and its L2.
-  const int pid = blockIdx.x;
-  const int n = a.n_work * a.nsplit;
+  // Packed documents: blocks [0, n_work), numbered as usual, run the first document
+  // with rows in each (head, tile); the blocks after them, one per (head,
+  // document), run a document on the tile where it starts when an earlier document
+  // has rows there too, so that two documents sharing a tile run side by side.
+  const bool vslot1 = kVarlen && int(blockIdx.x) >= a.n_work;
+  const int pid = vslot1 ? int(blockIdx.x) - a.n_work : int(blockIdx.x);
+  const int n = kVarlen ? a.n_work : a.n_work * a.nsplit;
   const int per = n / kNumXcd, rem = n % kNumXcd;
   const int xcd = pid % kNumXcd, local = pid / kNumXcd;
-  const int logical = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-  if (a.nsplit == 1) {
-    process(logical, 0, n_iter_blk, -1);
+  const int logical =
+      vslot1 ? pid : xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  if constexpr (kVarlen) {
+    auto end_of = [&](int d) { return min(max(a.cu_q[d + 1], 0), a.Sq); };
+    auto start_of = [&](int d) { return min(max(a.cu_q[d], 0), a.Sq); };
+    if (vslot1) {
+      const int d = pid / a.H, h = pid % a.H;
+      const int s0 = start_of(d);
+      if (end_of(d) <= s0) return;  // no rows
+      const int t = s0 / C::BM;
+      // rows of earlier documents in the tile: the packed rows [max(cu_q[0], tile start), s0)
+      if (max(start_of(0), t * C::BM) >= s0) return;  // the tile's first document: run below
+      process(h * a.m_tiles + t, 0, 0, -1, d);
+    } else {
+      // The tile's first document with rows in it: the first whose end lies past the
+      // tile's first row (binary search; the boundaries are non-decreasing), past
+      // empty ones.
+      const int r0 = (logical % a.m_tiles) * C::BM;
+      int lo = 0, hi = a.B;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (end_of(mid) > r0) hi = mid;
+        else lo = mid + 1;
+      }
+      while (lo < a.B && end_of(lo) <= start_of(lo) && start_of(lo) < r0 + C::BM) ++lo;
+      if (lo < a.B && start_of(lo) < r0 + C::BM && end_of(lo) > start_of(lo)) process(logical, 0, 0, -1, lo);
+    }
+  } else if (a.nsplit == 1) {
+    process(logical, 0, n_iter_blk, -1, 0);
   } else {
     const int j = logical % a.nsplit;
-    process(logical / a.nsplit, n_iter_blk * j / a.nsplit, n_iter_blk * (j + 1) / a.nsplit, logical);
+    process(logical / a.nsplit, n_iter_blk * j / a.nsplit, n_iter_blk * (j + 1) / a.nsplit, logical, 0);
   }
 }
 
@@ -991,6 +1064,19 @@ using namespace cpattn;
 
 namespace {
 
+// Local boundary i of an AllGather-KV rank whose query span is [s0, s0 + S_local):
+// the global boundary clamped into the span and shifted to it.  Document i's local
+// rows [local[i], local[i+1]) are then its intersection with the span, empty
+// when the two do not meet.
+__global__ void __launch_bounds__(256) remap_cu_kernel(const int* cu, int* local, int n, long long s0,
+                                                       long long S_local) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    const long long x = (long long)cu[i] - s0;
+    local[i] = int(x < 0 ? 0 : (x > S_local ? S_local : x));
+  }
+}
+
 View plain_view(int64_t S, int64_t H, int64_t D) {
   View v;
   v.bs = S * H * D;
@@ -1024,10 +1110,12 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
                 size_t ext_o, cp_stream_t stream, float* o_part = nullptr, float* lse = nullptr,
                 const float* st_o = nullptr, const float* st_lse = nullptr,
                 const __bf16* k1 = nullptr, const __bf16* v1 = nullptr, const uint8_t* mask1 = nullptr,
-                int64_t Skv1 = 0, const View* kv1 = nullptr) {
+                int64_t Skv1 = 0, const View* kv1 = nullptr, const int* cu_q = nullptr,
+                const int* cu_k = nullptr) {
   const int64_t bm = 32 * kGroupWaves;
   const int64_t m_tiles = (Sq + bm - 1) / bm;
-  const int64_t n_work = B * H * m_tiles;
+  // packed documents: B documents, one block per (head, tile of the packed rows)
+  const int64_t n_work = (cu_q ? 1 : B) * H * m_tiles;
   AttnArgs args;
   args.qv = qv;
   args.kv = kv;
@@ -1065,11 +1153,13 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
   args.lse = lse;
   args.st_o = st_o;
   args.st_lse = st_lse;
+  args.cu_q = cu_q;
+  args.cu_k = cu_k;
   // Split the key range of every query block into nsplit parts when the query
   // blocks alone would occupy at most half of the compute units; each part
   // keeps at least kMinSplitIters iterations.
   constexpr int64_t kMinSplitIters = 4;
-  if (ws) {
+  if (ws && !cu_q) {
     const int64_t cus = num_cus();
     const int64_t nsplit = std::min<int64_t>(cus / n_work, args.n_iter_blk / kMinSplitIters);
     if (2 * n_work <= cus && nsplit >= 2) {
@@ -1087,7 +1177,7 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // combine: BM * D / 4 threads of 256 per query block
-  const dim3 grid{unsigned(n_work * args.nsplit)}, block{unsigned(kThreads)}, cblock{256u},
+  const dim3 grid{unsigned(n_work * args.nsplit + (cu_q ? H * B : 0))}, block{unsigned(kThreads)}, cblock{256u},
       cgrid{unsigned(n_work * (D / 8))};
   // The chunked variants address rows through the views at run time (a view that
   // is not chunked is plain there too).  Segment 1 takes a view of its own when it
@@ -1098,10 +1188,11 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
   const int mode = (chunked ? kModeChunked : 0) | (seg1 ? kModeTwoSeg : 0) |
                    ((kv.chunked && kv.L.d % 64 != 0) || (seg1 && args.kv1.chunked && args.kv1.L.d % 64 != 0)
                         ? kModeCross : 0) |
-                   (seg1_rows ? kModeSeg1Rows : 0);
+                   (seg1_rows ? kModeSeg1Rows : 0) | (cu_q ? kModeVarlen : 0);
   auto launch_fwd = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, args); };
   if (D == 128) {
     if (mode == 0) launch_fwd(attn_fwd_kernel<128, 0>);
+    else if (mode == kModeVarlen) launch_fwd(attn_fwd_kernel<128, kModeVarlen>);
     else if (mode == kModeChunked) launch_fwd(attn_fwd_kernel<128, kModeChunked>);
     else if (mode == kModeChunked + kModeCross) launch_fwd(attn_fwd_kernel<128, kModeChunked + kModeCross>);
     else if (mode == kModeTwoSeg) launch_fwd(attn_fwd_kernel<128, kModeTwoSeg>);
@@ -1114,6 +1205,7 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
     if (args.nsplit > 1) hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, cblock, 0, s, args);
   } else {
     if (mode == 0) launch_fwd(attn_fwd_kernel<64, 0>);
+    else if (mode == kModeVarlen) launch_fwd(attn_fwd_kernel<64, kModeVarlen>);
     else if (mode == kModeChunked) launch_fwd(attn_fwd_kernel<64, kModeChunked>);
     else if (mode == kModeChunked + kModeCross) launch_fwd(attn_fwd_kernel<64, kModeChunked + kModeCross>);
     else if (mode == kModeTwoSeg) launch_fwd(attn_fwd_kernel<64, kModeTwoSeg>);
@@ -1178,6 +1270,53 @@ extern "C" int cp_attn_localq_globalkv_ws(const void* q, const void* k, const vo
                                           int64_t Skv, int64_t H, int64_t D, float scale, int causal,
                                           void* workspace, size_t workspace_bytes, cp_stream_t stream) {
   return attn_run(q, k, v, key_mask, o, B, Sq, Skv, H, D, scale, causal, workspace, workspace_bytes, stream);
+}
+
+extern "C" int cp_varlen_remap_cu_seqlens_q(const int32_t* cu_q_global, int32_t* cu_q_local, int64_t n_docs,
+                                            int64_t rank, int64_t S_local, cp_stream_t stream) {
+  if (!cu_q_global || !cu_q_local) return CP_ERR_NULL;
+  constexpr int64_t kIntMax = 0x7fffffff;
+  if (n_docs < 1 || n_docs >= kIntMax || rank < 0 || S_local < 1 || S_local > kIntMax ||
+      rank > kIntMax / S_local)
+    return CP_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(cu_q_global) | reinterpret_cast<uintptr_t>(cu_q_local)) & 3u)
+    return CP_ERR_ALIGNMENT;
+  const size_t bytes = size_t(n_docs + 1) * 4;
+  if (overlaps(cu_q_local, bytes, cu_q_global, bytes)) return CP_ERR_ALIAS;
+  const unsigned n = unsigned(n_docs + 1);
+  hipLaunchKernelGGL(remap_cu_kernel, dim3((n + 255) / 256), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     cu_q_global, cu_q_local, int(n), (long long)(rank * S_local), (long long)S_local);
+  return hip_status(hipGetLastError());
+}
+
+extern "C" int cp_attn_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int64_t n_docs, void* o,
+                              int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale, int causal,
+                              cp_stream_t stream) {
+  if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return CP_ERR_NULL;
+  if (const int st = attn_check(1, Sq, Skv, H, D, scale, causal)) return st;
+  constexpr int64_t kIntMax = 0x7fffffff;
+  if (n_docs < 1 || n_docs >= kIntMax) return CP_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return CP_ERR_ALIGNMENT;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) | reinterpret_cast<uintptr_t>(cu_seqlens_k)) & 3u)
+    return CP_ERR_ALIGNMENT;
+  if (Sq > kIntMax || Skv > kIntMax - 64 || H > kIntMax) return CP_ERR_SHAPE;
+  if (H * D * 2 * 64 > kIntMax) return CP_ERR_SHAPE;
+  const int64_t bm = 32 * kGroupWaves;
+  int64_t bh, n_work, qe, ke;
+  // one block per (head, tile) and one per (head, document)
+  if (!mul_capped(H, (Sq + bm - 1) / bm + n_docs, kIntMax, &n_work)) return CP_ERR_SHAPE;
+  (void)bh;
+  if (!mul_capped(Sq, H * D, int64_t(1) << 60, &qe) || !mul_capped(Skv, H * D, int64_t(1) << 60, &ke))
+    return CP_ERR_SHAPE;
+  const size_t qb = size_t(qe) * 2, kb = size_t(ke) * 2, cb = size_t(n_docs + 1) * 4;
+  if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb) ||
+      overlaps(o, qb, cu_seqlens_q, cb) || overlaps(o, qb, cu_seqlens_k, cb))
+    return CP_ERR_ALIAS;
+  return attn_launch(static_cast<const __bf16*>(q), plain_view(Sq, H, D), static_cast<const __bf16*>(k),
+                     static_cast<const __bf16*>(v), plain_view(Skv, H, D), nullptr, static_cast<__bf16*>(o),
+                     plain_view(Sq, H, D), n_docs, Sq, Skv, H, D, scale, nullptr, 0, qb, kb, qb, stream, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr, cu_seqlens_q, cu_seqlens_k);
 }
 
 extern "C" int cp_attn_joint(const void* q, const void* k_img, const void* v_img, const uint8_t* img_mask,

@@ -442,6 +442,54 @@ def cp_attn_recv_to_send_2d(recv, k_other, v_other, B: int, W: int, other_first:
     return out
 
 
+def cp_varlen_remap_cu_seqlens_q(cu_q_global, rank: int, S_local: int, out=None, stream=None) -> torch.Tensor:
+    """Local packed query boundaries of AllGather-KV rank ``rank`` (span
+    ``[rank*S_local, (rank+1)*S_local)``): int32 [n_docs + 1] on the device, one
+    (possibly empty) entry per global document; computed on the device."""
+    lib = _lib.load()
+    if cu_q_global.dtype != torch.int32 or cu_q_global.dim() != 1 or cu_q_global.numel() < 2:
+        raise ValueError("cu_q_global must be int32 [n_docs + 1], n_docs >= 1")
+    if out is None:
+        out = torch.empty_like(cu_q_global)
+    if out.dtype != torch.int32 or tuple(out.shape) != tuple(cu_q_global.shape):
+        raise ValueError("out must match cu_q_global")
+    _lib.check("cp_varlen_remap_cu_seqlens_q", lib.cp_varlen_remap_cu_seqlens_q(
+        _dev(cu_q_global, "cu_q_global"), _dev(out, "cu_q_local"), cu_q_global.numel() - 1, int(rank),
+        int(S_local), _stream(stream)))
+    return out
+
+
+def cp_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, out=None,
+                   causal=False, stream=None) -> torch.Tensor:
+    """Packed variable-length attention: q [Sq, H, D], k / v [Skv, H, D] bf16; query
+    document i (rows cu_seqlens_q[i]..cu_seqlens_q[i+1]) attends to key document i
+    only.  The boundary arrays are int32 device tensors of n_docs + 1 entries.
+    Rows of ``out`` outside every document are not written (a new ``out`` starts
+    at zero)."""
+    lib = _lib.load()
+    if q.dim() != 3 or k.dim() != 3 or tuple(k.shape) != tuple(v.shape) or q.shape[1:] != k.shape[1:]:
+        raise ValueError("expected q [Sq, H, D] and k, v [Skv, H, D]")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("attention takes bfloat16")
+    for name, c in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if c.dtype != torch.int32 or c.dim() != 1 or c.numel() < 2:
+            raise ValueError(f"{name} must be int32 [n_docs + 1], n_docs >= 1")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must describe the same documents")
+    Sq, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.zeros_like(q)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    _lib.check("cp_attn_varlen", lib.cp_attn_varlen(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(cu_seqlens_q, "cu_seqlens_q"),
+        _dev(cu_seqlens_k, "cu_seqlens_k"), cu_seqlens_q.numel() - 1, _dev(out, "o"),
+        Sq, k.shape[0], H, D, float(scale), int(bool(causal)), _stream(stream)))
+    return out
+
+
 def cp_attn_workspace_bytes(B: int, Sq: int, Skv: int, H: int, D: int) -> int:
     """Workspace bytes cp_attn_localq_globalkv may use with split=True (upper bound, current device)."""
     return int(_lib.load().cp_attn_workspace_bytes(B, Sq, Skv, H, D))

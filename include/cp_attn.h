@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CP_ABI_VERSION 8
+#define CP_ABI_VERSION 9
 
 typedef struct ihipStream_t* cp_stream_t; /* == hipStream_t */
 
@@ -396,6 +396,59 @@ int cp_attn_recv_to_send_2d(const void* recv, const void* k_other, const void* v
 int cp_output_reverse(int phase, const void* src, void* dst,
                       int64_t B, int64_t S_local, int64_t H_local, int64_t D, int64_t W,
                       int dtype, cp_stream_t stream);
+
+/*
+ * Packed query boundaries of one AllGather-KV rank ([vllm-omni#7641], review-fix
+ * commit on packed query metadata).  Packed documents (requests) share one
+ * sequence; cu_seqlens holds their n_docs + 1 cumulative boundaries.  After the
+ * K/V gather a rank keeps only the query rows [rank*S_local, (rank+1)*S_local),
+ * so every global query document is intersected with that span: entry i of the
+ * result is boundary i clamped into the span and shifted to it,
+ *
+ *   cu_q_local[i] = min(max(cu_q_global[i] - rank*S_local, 0), S_local),
+ *
+ * which keeps exactly one, possibly empty, local entry per document (query
+ * document i still pairs with key document i; the key boundaries stay global).
+ * The remap runs on the device, in stream order, with no host synchronisation.
+ *
+ *   cu_q_global : [n_docs + 1] int32, device, non-decreasing
+ *   cu_q_local  : [n_docs + 1] int32, device, output; disjoint from cu_q_global
+ *
+ * Requires n_docs >= 1, rank >= 0, S_local >= 1 with rank*S_local and
+ * S_local within int32 (CP_ERR_SHAPE), 4-byte aligned pointers.
+ */
+int cp_varlen_remap_cu_seqlens_q(const int32_t* cu_q_global, int32_t* cu_q_local, int64_t n_docs,
+                                 int64_t rank, int64_t S_local, cp_stream_t stream);
+
+/*
+ * Packed variable-length attention (the packed backend of [vllm-omni#7641]'s
+ * review-fix commit on packed query metadata, on the AllGather-KV rank's local
+ * query rows).  One packed batch row: query document i takes rows
+ * [cu_seqlens_q[i], cu_seqlens_q[i+1]) of q and attends, non-causally, to the
+ * key rows [cu_seqlens_k[i], cu_seqlens_k[i+1]) of k and v only:
+ * softmax(scale q k^T) v per document and head.
+ *
+ *   q, o           : [Sq][H][D] bf16 (o disjoint from every input)
+ *   k, v           : [Skv][H][D] bf16
+ *   cu_seqlens_q/k : [n_docs + 1] int32, device, non-decreasing, within
+ *                    [0, Sq] and [0, Skv] (read by the kernel and not checked on
+ *                    the host; out-of-range values are clamped into the buffers,
+ *                    so a malformed array gives wrong rows, never an access
+ *                    outside them)
+ *
+ * The work is one block per (head, 128-row tile of the packed query rows), which
+ * finds the tile's first document by binary search on cu_seqlens_q, and one per
+ * (head, document), which runs the document on the tile where it starts when an
+ * earlier document has rows there too; no max_seqlen_q is needed.  A document with query rows and no key
+ * rows gets zero outputs.  Rows of o outside every document are not written (the
+ * one exception to "outputs are fully overwritten").  No key mask, no split; D in
+ * {64, 128}, causal == 0, 16-byte aligned q, k, v, o and 4-byte aligned boundary
+ * arrays; n_docs >= 1.
+ */
+int cp_attn_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                   const int32_t* cu_seqlens_k, int64_t n_docs, void* o,
+                   int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale, int causal,
+                   cp_stream_t stream);
 
 #ifdef __cplusplus
 }

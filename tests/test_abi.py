@@ -129,6 +129,20 @@ def _fused2d(**kw):
                                                a["causal"], a["ws"], a["nbytes"], None)
 
 
+def _varlen(**kw):
+    a = dict(q=A, k=A + BIG, v=A + 2 * BIG, cq=A + 3 * BIG, ck=A + 4 * BIG, n=2, o=A + 5 * BIG, Sq=100,
+             Skv=200, H=2, D=128, scale=0.125, causal=0)
+    a.update(kw)
+    return _lib.load().cp_attn_varlen(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["n"], a["o"], a["Sq"],
+                                      a["Skv"], a["H"], a["D"], a["scale"], a["causal"], None)
+
+
+def _remap(**kw):
+    a = dict(g=A, l=A + BIG, n=3, r=1, Sl=16)
+    a.update(kw)
+    return _lib.load().cp_varlen_remap_cu_seqlens_q(a["g"], a["l"], a["n"], a["r"], a["Sl"], None)
+
+
 def _partial(**kw):
     a = dict(q=A, k=A + BIG, v=A + 2 * BIG, m=None, o=A + 3 * BIG, lse=A + 4 * BIG, B=1, Sq=8, Skv=16,
              H=2, D=128, scale=0.125, causal=0)
@@ -291,6 +305,43 @@ def test_recv_to_send_rejects(kw, code):
 ])
 def test_recv_to_send_2d_rejects(kw, code):
     assert _fused2d(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.CP_ERR_NULL),
+    (dict(cq=None), _lib.CP_ERR_NULL),
+    (dict(ck=None), _lib.CP_ERR_NULL),
+    (dict(n=0), _lib.CP_ERR_SHAPE),
+    (dict(Sq=0), _lib.CP_ERR_SHAPE),
+    (dict(Skv=0), _lib.CP_ERR_SHAPE),
+    (dict(H=1 << 24), _lib.CP_ERR_SHAPE),             # a K/V tile's rows beyond 32-bit offsets
+    (dict(D=96), _lib.CP_ERR_HEAD_DIM),
+    (dict(scale=0.0), _lib.CP_ERR_SCALE),
+    (dict(causal=1), _lib.CP_ERR_UNSUPPORTED),
+    (dict(o=A + 5 * BIG + 8), _lib.CP_ERR_ALIGNMENT),
+    (dict(cq=A + 3 * BIG + 2), _lib.CP_ERR_ALIGNMENT),
+    (dict(o=A + 64), _lib.CP_ERR_ALIAS),              # o over q
+    (dict(o=A + 2 * BIG + 16), _lib.CP_ERR_ALIAS),    # o over v
+    (dict(ck=A + 5 * BIG + 4), _lib.CP_ERR_ALIAS),    # key boundaries inside o
+])
+def test_varlen_rejects(kw, code):
+    assert _varlen(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(g=None), _lib.CP_ERR_NULL),
+    (dict(l=None), _lib.CP_ERR_NULL),
+    (dict(n=0), _lib.CP_ERR_SHAPE),
+    (dict(r=-1), _lib.CP_ERR_SHAPE),
+    (dict(Sl=0), _lib.CP_ERR_SHAPE),
+    (dict(r=1 << 20, Sl=1 << 12), _lib.CP_ERR_SHAPE),  # span start beyond int32
+    (dict(l=A + BIG + 2), _lib.CP_ERR_ALIGNMENT),
+    (dict(l=A + 8), _lib.CP_ERR_ALIAS),
+])
+def test_remap_rejects(kw, code):
+    assert _remap(**kw) == code
 
 
 @cpu_only

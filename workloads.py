@@ -149,6 +149,14 @@ def text_lengths(wl: Workload) -> np.ndarray:
     return rng.integers(wl.text_len_min, wl.text_len_max + 1, size=wl.B)
 
 
+def packed_boundaries(wl, n_docs):
+    """Seeded boundaries of ``n_docs`` documents packed into the ``wl.S`` rows of one
+    batch row: ``[0, c_1, ..., wl.S]`` with distinct cut points drawn uniformly."""
+    rng = np.random.default_rng(wl.seed + 31)
+    cuts = np.sort(rng.choice(np.arange(1, wl.S), size=n_docs - 1, replace=False))
+    return [0] + [int(c) for c in cuts] + [wl.S]
+
+
 def key_mask(wl: Workload, text_front: bool = False) -> np.ndarray | None:
     """uint8 ``[B, S]`` key-validity mask (nonzero = attend), or None when unmasked.
 

@@ -138,3 +138,28 @@ def test_agkv_ranks_reassemble_unsplit(gu, A, S, H, D, cu):
     ref = np.concatenate(OV.agkv_varlen_outputs(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v),
                                                 cu, A, 1.0 / math.sqrt(D)), axis=0)
     _close(gu.to_f64(cat), ref, "AllGather-KV varlen")
+
+
+def test_full_size_image_share_all_ranks(gu):
+    """The bench's packed workload at full size: the image CP4 sequence (4352 rows, 24
+    heads, D 128) cut into 4 seeded documents, every AllGather-KV rank's remap and
+    packed attention of its 1088 rows, against the oracle over every output."""
+    import context_attention_diffusion_amd as cp
+    import workloads
+    wl = workloads.WORKLOADS["image_cp4"]
+    cu = workloads.packed_boundaries(wl, 4)
+    print(f"[varlen] full size image_cp4, documents {cu}", flush=True)
+    q, k, v = (np.ascontiguousarray(t[0]) for t in workloads.global_qkv(wl))
+    qd, kd, vd = gu.to_dev(q), gu.to_dev(k), gu.to_dev(v)
+    g = _cu(gu, cu)
+    Sl = wl.attn_rows
+    A = wl.S // Sl
+    parts = []
+    for r in range(A):
+        loc = cp.cp_varlen_remap_cu_seqlens_q(g, r, Sl)
+        parts.append(cp.cp_attn_varlen(qd[r * Sl:(r + 1) * Sl].contiguous(), kd, vd, loc, g))
+    torch.cuda.synchronize()
+    got = gu.to_f64(torch.cat(parts, dim=0))
+    ref = np.concatenate(OV.agkv_varlen_outputs(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v),
+                                                cu, A, 1.0 / math.sqrt(wl.D)), axis=0)
+    _close(got, ref, "image_cp4 packed, 4 ranks")

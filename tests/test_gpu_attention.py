@@ -323,6 +323,42 @@ def test_recv_to_send_full_size_sampled(gu, name):
     _assert_close(sel, ref, f"recv_to_send {name} sampled")
 
 
+@pytest.mark.parametrize("a", [0, 1])
+def test_recv_to_send_2d_full_size_sampled(gu, a):
+    """The video 2D layout (U 2 x A 2) at full size, Ulysses rank u = 0 of AllGather
+    index a: the received buffer of its Ulysses group and the other AllGather rank's
+    resident K/V of the same heads; the whole send buffer against the unfused chain,
+    sampled rows against the oracle."""
+    import context_attention_diffusion_amd as cp
+    from oracle import layout as OL
+    wl = workloads.WORKLOADS["video_u2a2"]
+    U, A, Sl, D = wl.W, wl.A, wl.S_local, wl.D
+    Hl = wl.H // U
+    full = workloads.global_qkv(wl)
+    reg = U * Sl   # rows of one AllGather region
+    shards = [tuple(np.ascontiguousarray(t[:, (a * U + r) * Sl:(a * U + r + 1) * Sl]) for t in full)
+              for r in range(U)]
+    recv0 = OL.exchange([OL.pack_qkv_dst_major(*shards[r], U) for r in range(U)])[0]
+    o_reg = slice((1 - a) * reg, (2 - a) * reg)
+    ko, vo = (np.ascontiguousarray(t[:, o_reg, :Hl]) for t in full[1:])
+    rd, kd, vd = gu.to_dev(recv0), gu.to_dev(ko), gu.to_dev(vo)
+    print(f"[attn] recv_to_send_2d full video_u2a2 a={a}", flush=True)
+    got = cp.cp_attn_recv_to_send_2d(rd, kd, vd, 1, U, other_first=(a == 1))
+    q, k, v = cp.cp_unpack_head_sharded(rd, 1, U)
+    o = cp.cp_attn_joint(q, k, v, kd, vd, None, None, joint_front=(a == 1))
+    ref_gpu = cp.cp_output_reverse(0, o, U, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref_gpu)
+    # rank (a, 0): query rows of region a, heads [0, Hl), against every key row of those heads
+    qf, kf, vf = (bf16.bits_to_f64(np.ascontiguousarray(t[:, :, :Hl])) for t in full)
+    rng = np.random.default_rng(wl.seed + 11 + a)
+    rows = [(0, int(rng.integers(reg)), int(rng.integers(Hl))) for _ in range(24)]
+    ref = OA.attention_rows(qf[:, a * reg:(a + 1) * reg], kf, vf, rows, None, 1.0 / math.sqrt(D))
+    g = gu.to_f64(got)
+    sel = np.stack([g[i // Sl, 0, i % Sl, h] for _, i, h in rows])
+    _assert_close(sel, ref, f"recv_to_send_2d video a={a} sampled")
+
+
 # ------------------------------------------ attention over K/V chunks, then merge
 
 # The row sum adds bf16-rounded probabilities (each within 2^-9 relative of the

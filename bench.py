@@ -784,7 +784,17 @@ def summarize_traffic(fetch_dir, write_dir, out_json, workload):
            "fetch_kib_raw": f_attn, "write_kib_raw": w_attn,
            "copy_fetch_kib_raw": f_copy, "copy_write_kib_raw": w_copy,
            "scale_fetch": sf, "scale_write": sw,
-           "traffic_bytes": (f_attn * sf + w_attn * sw) * 1024.0}
+           "traffic_bytes": (f_attn * sf + w_attn * sw) * 1024.0,
+           "commands": [
+               f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir}/attn -o p --output-format csv -- python3 bench.py "
+               f"--workload {workload} --only attn --steps 5 --warmup 1 --eager",
+               f"rocprofv3 --pmc WRITE_SIZE -d {write_dir}/attn -o p --output-format csv -- python3 bench.py "
+               f"--workload {workload} --only attn --steps 5 --warmup 1 --eager",
+               f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir}/copy -o p --output-format csv -- python3 bench.py "
+               "--calib-copy",
+               f"rocprofv3 --pmc WRITE_SIZE -d {write_dir}/copy -o p --output-format csv -- python3 bench.py "
+               "--calib-copy",
+               f"python3 bench.py --workload {workload} --summarize-traffic {fetch_dir} {write_dir} {out_json}"]}
     with open(out_json, "w") as fh:
         json.dump(res, fh, indent=1)
     print(json.dumps(res))

@@ -48,6 +48,17 @@
 //    applied only to tiles that need it.
 //  * Workgroups are numbered so that all query tiles of one (batch, head) land
 //    on the same XCD, whose L2 then serves that head's K/V to all of them.
+//
+// Variants (compile-time MODE bits, so that the dense path carries none of the
+// others' scalar state): 1 = operands addressed through strided views whose
+// rows may come in chunks (Q/K/V read from a received Ulysses buffer, O written
+// in the send layout); 4 = with chunks whose length is not a multiple of the
+// 64-key tile (tiles spanning chunks take per-lane row offsets); 2 = keys in two
+// segments with masks of their own (joint text/image keys, or the other
+// AllGather rank's K/V); 8 = a second segment with a row stride of its own;
+// 16 = packed documents (varlen: query document i against key document i, the
+// boundaries read from device memory).  Split-KV and the partial / accumulating
+// outputs are run-time paths of the same kernel, with a separate merge kernel.
 
 #include <hip/hip_runtime.h>
 

@@ -40,12 +40,19 @@ over the whole sequence, the same FLOPs) timed once with separate unpack and
 send steps and once with cp_attn_recv_to_send, which reads Q/K/V from the
 received buffer and writes the send layout directly.
 
-Prints one JSON line.  `value` is attention TFLOP/s over the whole step
-(algorithmic attention FLOPs / step time), with the step captured once into a
-HIP graph and replayed (`--eager` launches it op by op).  Per-kernel durations
-come from HIP events on the launch stream around HIP-graph replays of a burst
-of up to 100 back-to-back launches of each kernel on the step's own buffers
-(three warm-up launches, one untimed replay, the median of three timed ones).
+Prints one JSON line.  The headline workload is video_u2a2 (the largest
+one-GPU share: 16380 queries x 32760 keys, 6 heads).  `value` is attention
+TFLOP/s over the whole step (algorithmic attention FLOPs / step time), with the
+step captured once into a HIP graph and replayed (`--eager` launches it op by
+op).  Per-kernel durations come from HIP events on the launch stream around
+HIP-graph replays of a burst of 100 back-to-back launches of each kernel on the
+step's own buffers (three warm-up launches, one untimed replay, the median of
+three timed ones), after about a second of step replays that brings the clock
+to its loaded level; neither depends on --steps.  `per_config` repeats the
+per-kernel measurement, the cold layout pass and the whole-output parity check
+for the other workloads.  `cpu_baseline` times the fp64 oracle over the
+headline's whole attention problem on the host cores, and `parity` compares
+every element of the GPU output with that oracle result.
 """
 
 from __future__ import annotations
@@ -65,7 +72,12 @@ sys.path.insert(0, ROOT)
 METRIC = "attn TFLOP/s + % bf16 MFMA peak (local-Q/global-KV); pack/unpack HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
-DEFAULT_WORKLOAD = "image_cp4"
+DEFAULT_WORKLOAD = "video_u2a2"
+# Configurations measured beside the headline, each the same way (kernel bursts, cold
+# layout, parity), reported under "per_config".
+PER_CONFIG = ("image_cp4", "image_cp8", "joint_cfg_cp4", "tiny_w2")
+KERNEL_BURST = 100             # launches per timed HIP-graph replay, whatever --steps is
+CLOCK_WARMUP_S = 1.0           # replays of the step before the per-kernel bursts
 
 
 def parse():
@@ -75,7 +87,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-budget-s", type=float, default=10.0)
+    p.add_argument("--no-per-config", action="store_true",
+                   help="measure the headline workload only (no per_config section)")
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache pack/unpack pass")
     p.add_argument("--eager", action="store_true",
                    help="launch the timed steps one by one instead of replaying a captured HIP graph")
@@ -88,6 +101,9 @@ def parse():
                    help="turn one rocprofv3 --pmc run of this bench (SQ_VALU_MFMA_BUSY_CYCLES, "
                         "SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_BUSY_CU_CYCLES, GRBM_GUI_ACTIVE) into an MFMA "
                         "utilisation summary of the attention kernel; no GPU work")
+    p.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DB", "OUT_MD", "COMMAND"),
+                   help="turn a rocprofv3 --kernel-trace --stats database of a run of this bench into a "
+                        "per-kernel summary (COMMAND: the profiled command line, quoted); no GPU work")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the fused-chain, chunked-K/V and joint-segment sections (so a kernel "
                         "trace of the run holds only the headline step's launches)")
@@ -284,41 +300,7 @@ def cold_layout_gbps(wl, dev, rounds=4):
     return res
 
 
-def cpu_baseline(wl, full, mask, budget_s):
-    """The oracle's attention timed on the host cores over the first n query rows of the
-    rank's problem (n sized to about budget_s of CPU work)."""
-    from oracle import attention as OA
-    from oracle import bf16
-
-    if wl.A > 1:
-        q_all = full[0][:, :wl.attn_rows, :wl.attn_heads]
-    else:
-        q_all = full[0][:, :wl.attn_rows, :wl.attn_heads]
-    k = bf16.bits_to_f64(full[1][:, :, :wl.attn_heads])
-    v = bf16.bits_to_f64(full[2][:, :, :wl.attn_heads])
-    valid = wl.S if mask is None else None
-
-    def flops(n):
-        if mask is None:
-            return 4.0 * wl.B * wl.attn_heads * n * wl.S * wl.D
-        return 4.0 * wl.attn_heads * n * wl.D * float(mask.astype(np.int64).sum())
-
-    n0 = min(wl.attn_rows, 16)
-    OA.attention(bf16.bits_to_f64(q_all[:, :n0]), k, v, mask, 1.0 / math.sqrt(wl.D))   # warm-up
-    n1 = min(wl.attn_rows, 4 * n0)
-    q1 = bf16.bits_to_f64(q_all[:, :n1])
-    t = time.perf_counter()
-    OA.attention(q1, k, v, mask, 1.0 / math.sqrt(wl.D))
-    t1 = time.perf_counter() - t
-    n = int(min(wl.attn_rows, max(n1, n1 * budget_s / max(t1, 1e-6))))
-    q = bf16.bits_to_f64(q_all[:, :n])
-    # When the whole problem is quicker than the budget, repeat it (up to 30 times).
-    est = t1 * n / n1
-    reps = int(max(1, min(30, budget_s // max(est, 1e-6))))
-    t = time.perf_counter()
-    for _ in range(reps):
-        OA.attention(q, k, v, mask, 1.0 / math.sqrt(wl.D))
-    dt = (time.perf_counter() - t) / reps
+def blas_threads():
     threads = os.cpu_count()
     try:
         from threadpoolctl import threadpool_info
@@ -327,45 +309,64 @@ def cpu_baseline(wl, full, mask, budget_s):
             threads = max(int(x.get("num_threads", 1)) for x in info)
     except Exception:
         pass
-    del valid
+    return threads
+
+
+def oracle_attention(wl, full, mask):
+    """The fp64 oracle over the rank's whole attention problem (query rows [0, attn_rows),
+    heads [0, attn_heads), every key); returns (output, seconds)."""
+    from oracle import attention as OA
+    from oracle import bf16
+
+    q = bf16.bits_to_f64(np.ascontiguousarray(full[0][:, :wl.attn_rows, :wl.attn_heads]))
+    k = bf16.bits_to_f64(np.ascontiguousarray(full[1][:, :, :wl.attn_heads]))
+    v = bf16.bits_to_f64(np.ascontiguousarray(full[2][:, :, :wl.attn_heads]))
+    t = time.perf_counter()
+    ref = OA.attention(q, k, v, mask, 1.0 / math.sqrt(wl.D))
+    return ref, time.perf_counter() - t
+
+
+def cpu_baseline(wl, flops, seconds):
     return {
-        "value": flops(n) / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": f"fp64 oracle attention over query rows [0,{n}) of {wl.attn_rows}, "
-                  f"{wl.attn_heads} heads, all {wl.S} keys, B={wl.B}; {reps} pass(es) of {dt:.2f} s; "
+        "value": flops / seconds / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+        "sample": f"fp64 oracle attention over the whole rank problem: query rows [0,{wl.attn_rows}), "
+                  f"{wl.attn_heads} heads, all {wl.S} keys, B={wl.B}; one pass of {seconds:.2f} s; "
                   f"host cpu_count={os.cpu_count()}",
     }
 
 
-def parity_sample(path, wl, nrows=24):
-    """Quick parity figures for the report (the full parity suite lives in tests/)."""
-    from oracle import attention as OA
-    from oracle import bf16
-    from oracle import layout as OL
-
+def parity_whole(path, wl, ref):
+    """Every element of the step's attention output against the oracle result, and the
+    unpacked Q against its closed form (head slice 0 of the group's sequence)."""
     import torch
 
     torch.cuda.synchronize()
-    res = {}
-    # unpack output vs the closed form (head slice 0 of the group's sequence)
     Hl = wl.H // wl.W
     span = wl.W * wl.S_local
     got = path.q_hs.view(torch.int16).cpu().numpy().view(np.uint16)
-    res["unpack_q_bit_exact"] = bool(np.array_equal(got, path.full[0][:, :span, :Hl]))
-    del OL
-    rng = np.random.default_rng(wl.seed)
-    rows = [(int(rng.integers(wl.B)), int(rng.integers(wl.attn_rows)), int(rng.integers(wl.attn_heads)))
-            for _ in range(nrows)]
-    q = path.full[0][:, :wl.attn_rows, :wl.attn_heads]
-    ref = OA.attention_rows(bf16.bits_to_f64(q), bf16.bits_to_f64(path.full[1][:, :, :wl.attn_heads]),
-                            bf16.bits_to_f64(path.full[2][:, :, :wl.attn_heads]), rows,
-                            path.mask_np, 1.0 / math.sqrt(wl.D))
     o = path.o_attn.float().cpu().numpy().astype(np.float64)
-    sel = np.stack([o[b, i, h] for b, i, h in rows])
-    err = np.abs(sel - ref)
-    res["attn_sampled_rows"] = nrows
-    res["attn_max_abs_err"] = float(err.max())
-    res["attn_mean_abs_err"] = float(err.mean())
-    return res
+    err = np.abs(o - ref)
+    return {"unpack_q_bit_exact": bool(np.array_equal(got, path.full[0][:, :span, :Hl])),
+            "attn_elements_compared": int(err.size),
+            "attn_max_abs_err": float(err.max()), "attn_mean_abs_err": float(err.mean()),
+            "attn_within_tolerance": bool(err.max() <= 2e-2 and err.mean() <= 2e-3)}
+
+
+def warm_clock(fn, seconds=CLOCK_WARMUP_S):
+    """Run fn back to back for about `seconds` so that the timed bursts after it see the
+    clock the GPU settles at under load, not the idle clock of the first launches."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                break
+    torch.cuda.synchronize()
 
 
 def time_burst(fn, burst, repeats=3):
@@ -395,7 +396,7 @@ def time_burst(fn, burst, repeats=3):
     return float(np.median(times))
 
 
-def kernel_bursts(path, only=None, burst=20):
+def kernel_bursts(path, only=None, burst=KERNEL_BURST):
     """Average duration (ms) of each kernel of the step over `burst` back-to-back launches."""
     snd = path.send()
     launches = {
@@ -858,6 +859,37 @@ def summarize_mfma(pmc_dir, out_md, workload):
     print("\n".join(lines))
 
 
+def summarize_trace(db_path, out_md, command, workload):
+    """Per-kernel launch counts and durations from a rocprofv3 kernel-trace database
+    (its top_kernels view: durations in microseconds), with the attention kernel's
+    algorithmic TFLOP/s and fraction of the dense bf16 peak at that average."""
+    import sqlite3
+    import workloads
+    wl = workloads.WORKLOADS[workload]
+    mask = workloads.key_mask(wl)
+    flops = attn_flops(wl, mask)
+    con = sqlite3.connect(db_path)
+    rows = list(con.execute("select name, total_calls, total_duration, average, percentage from top_kernels"))
+    lines = [f"# Kernel trace: workload {workload}", "", "Command (repository root, one MI355X):", "", "```",
+             command, f"python3 bench.py --workload {workload} --summarize-trace <trace db> <this file> '<command>'",
+             "```", "", "| kernel | launches | total us | average us | share of GPU time |", "|---|---|---|---|---|"]
+    def short(name):
+        return name.replace("void ", "").replace("cpattn::(anonymous namespace)::", "").split("(")[0]
+
+    for name, n, tot, avg, pct in rows:
+        lines.append(f"| `{short(name)}` | {n} | {tot:.1f} | {avg:.3f} | {pct:.2f}% |")
+    attn = [r for r in rows if "attn_fwd_kernel" in r[0]]
+    if attn:
+        name, n, tot, avg, pct = max(attn, key=lambda r: r[2])
+        tf = flops / (avg * 1e-6) / 1e12
+        lines += ["", f"Attention (`{short(name)}`): {flops / 1e9:.2f} GFLOP per launch "
+                  f"(4 B H Sq Skv D over valid keys) / {avg:.2f} us average = {tf:.1f} TFLOP/s = "
+                  f"{100.0 * tf / PEAK_BF16_TFLOPS:.1f}% of the 2.5 PFLOP/s dense bf16 peak."]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def calib_copy():
     import torch
     a = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda:0").normal_()
@@ -879,6 +911,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma, args.workload)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.workload)
         return
     import torch
 
@@ -927,27 +962,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # Per-kernel durations: each kernel of the step launched `burst` times back to
-    # back on the launch stream between one pair of HIP events (same buffers as the
-    # step), three timed replays, the median kept.
-    kms = kernel_bursts(path, only=args.only, burst=max(5, min(100, args.steps)))
-
     flops = attn_flops(wl, path.mask_np)
-    pack_bytes, merge_bytes = wl.pack_bytes(), wl.merge_bytes()
-    kern = {}
-    if "attn" in kms:
-        t = kms["attn"] * 1e-3
-        kern["attn"] = {"us": kms["attn"] * 1e3, "TFLOPs": flops / t / 1e12,
-                        "frac_bf16_peak": flops / t / 1e12 / PEAK_BF16_TFLOPS,
-                        "flops": flops, "flops_dense": wl.attn_flops_dense()}
-    for name, nbytes in (("pack", pack_bytes), ("unpack", pack_bytes), ("merge", merge_bytes),
-                         ("exchange_in", pack_bytes), ("exchange_out", merge_bytes),
-                         ("send", merge_bytes)):
-        if name in kms:
-            t = kms[name] * 1e-3
-            kern[name] = {"us": kms[name] * 1e3, "GBps_warm": nbytes / t / 1e9,
-                          "frac_hbm_peak": nbytes / t / 1e9 / PEAK_HBM_GBPS, "bytes": nbytes}
-
     value = flops / (ms_per_step * 1e-3) / 1e12 if args.only in (None, "attn") else None
     out = {
         "metric": METRIC,
@@ -963,12 +978,75 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "B": wl.B, "S_global": wl.S, "H": wl.H, "D": wl.D,
-                   "W": wl.W, "A": wl.A, "S_local": wl.S_local,
-                   "attn_q": [wl.B, wl.attn_rows, wl.attn_heads, wl.D],
-                   "attn_kv": [wl.B, wl.S, wl.attn_heads, wl.D], "masked": wl.masked,
-                   "parallelism": "one rank's share, exchange simulated on one GPU"},
+        "config": config_of(wl),
     }
+    step_fn = graph.replay if graph is not None else (lambda: run_steps(path, 1, only=args.only))
+    rec = measure_config(path, args, step_fn)
+    if "roofline" in rec:
+        out["roofline"] = rec.pop("roofline")
+    out.update(rec)
+    if args.only is None:
+        ref, secs = oracle_attention(wl, path.full, path.mask_np)
+        out["parity"] = parity_whole(path, wl, ref)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(wl, flops, secs)
+        del ref
+    del graph, path
+    torch.cuda.empty_cache()
+    if args.only is None and not args.no_per_config:
+        per = {}
+        for name in PER_CONFIG:
+            if name == wl.name:
+                continue
+            w = workloads.WORKLOADS[name]
+            p = RankPath(w, dev)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_steps(p, 1)
+            g.replay()
+            torch.cuda.synchronize()
+            r = measure_config(p, args, g.replay)
+            r["config"] = config_of(w)
+            ref, _ = oracle_attention(w, p.full, p.mask_np)
+            r["parity"] = parity_whole(p, w, ref)
+            per[name] = r
+            del g, p, ref
+            torch.cuda.empty_cache()
+        out["per_config"] = per
+    print(json.dumps(out), flush=True)
+
+
+def config_of(wl):
+    return {"workload": wl.name, "B": wl.B, "S_global": wl.S, "H": wl.H, "D": wl.D,
+            "W": wl.W, "A": wl.A, "S_local": wl.S_local,
+            "attn_q": [wl.B, wl.attn_rows, wl.attn_heads, wl.D],
+            "attn_kv": [wl.B, wl.S, wl.attn_heads, wl.D], "masked": wl.masked,
+            "parallelism": "one rank's share, exchange simulated on one GPU"}
+
+
+def measure_config(path, args, step_fn):
+    """Per-kernel durations (after a clock warm-up of step replays), the attention's
+    roofline, the cold layout pass and the workload's extra sections."""
+    import torch
+    wl, dev = path.wl, path.dev
+    warm_clock(step_fn)
+    kms = kernel_bursts(path, only=args.only)
+    flops = attn_flops(wl, path.mask_np)
+    pack_bytes, merge_bytes = wl.pack_bytes(), wl.merge_bytes()
+    kern = {}
+    if "attn" in kms:
+        t = kms["attn"] * 1e-3
+        kern["attn"] = {"us": kms["attn"] * 1e3, "TFLOPs": flops / t / 1e12,
+                        "frac_bf16_peak": flops / t / 1e12 / PEAK_BF16_TFLOPS,
+                        "flops": flops, "flops_dense": wl.attn_flops_dense()}
+    for name, nbytes in (("pack", pack_bytes), ("unpack", pack_bytes), ("merge", merge_bytes),
+                         ("exchange_in", pack_bytes), ("exchange_out", merge_bytes),
+                         ("send", merge_bytes)):
+        if name in kms:
+            t = kms[name] * 1e-3
+            kern[name] = {"us": kms[name] * 1e3, "GBps_warm": nbytes / t / 1e9,
+                          "frac_hbm_peak": nbytes / t / 1e9 / PEAK_HBM_GBPS, "bytes": nbytes}
+    rec = {}
     if "attn" in kern:
         traffic = None
         tf = traffic_file(wl.name)
@@ -976,15 +1054,16 @@ def main():
             t = json.load(open(tf))
             if t.get("src_sha256") == src_sha256():   # counters taken on this kernel source
                 traffic = t["traffic_bytes"]
-        out["roofline"] = {"bound": "mfma", "achieved": kern["attn"]["TFLOPs"],
+        rec["roofline"] = {"bound": "mfma", "achieved": kern["attn"]["TFLOPs"],
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": kern["attn"]["TFLOPs"] / PEAK_BF16_TFLOPS, "traffic": traffic,
                            "kernel": "attn_fwd_kernel",
-                           "algorithmic_flops_per_launch": flops}
-    out["kernels"] = kern
+                           "algorithmic_flops_per_launch": flops,
+                           "launches_per_timed_replay": KERNEL_BURST}
+    rec["kernels"] = kern
     if args.only is None and not args.no_cold:
         pc, uc, cc = cold_layout_gbps(wl, dev)
-        out["layout_cold"] = {"pack_GBps": pc, "unpack_GBps": uc,
+        rec["layout_cold"] = {"pack_GBps": pc, "unpack_GBps": uc,
                               "pack_frac_hbm_peak": pc / PEAK_HBM_GBPS,
                               "unpack_frac_hbm_peak": uc / PEAK_HBM_GBPS,
                               "torch_copy_same_bytes_GBps": cc,
@@ -995,36 +1074,36 @@ def main():
         u["fused_step_TFLOPs"] = flops / (u["fused_step_us"] * 1e-6) / 1e12
         u["note"] = ("Ulysses-only rank step: attention of H/W heads over all W*S_l rows, "
                      "same FLOPs as the local-Q/global-KV share")
-        out["ulysses_fused"] = u
+        rec["ulysses_fused"] = u
         c = chunked_kv(path)
         c["total_us"] = c["partials_us"] + c["merge_us"]
         c["dense_us"] = kern["attn"]["us"] if "attn" in kern else None
+        if c["dense_us"]:
+            c["total_over_dense"] = c["total_us"] / c["dense_us"]
+            c["accumulate_over_dense"] = c["accumulate_us"] / c["dense_us"]
         c["note"] = ("local-Q/global-KV share with K/V in W chunks: W partial attentions "
                      "(fp32 O + lse) and one merge, against the dense call")
-        out["chunked_kv"] = c
+        rec["chunked_kv"] = c
     if args.only is None and path.two_d and not args.no_extras:
         u = ulysses_2d_chain(path)
         u["fused_attn_TFLOPs"] = flops / (u["fused_attn_us"] * 1e-6) / 1e12
         u["fused_step_TFLOPs"] = flops / (u["fused_step_us"] * 1e-6) / 1e12
         u["note"] = ("2D rank step: the unpack and the gathered-K/V attention against one fused call "
                      "over the received buffer and the other AllGather rank's resident K/V")
-        out["ulysses_2d_fused"] = u
+        rec["ulysses_2d_fused"] = u
     if args.only is None and not path.two_d and not wl.masked and wl.B == 1 and not args.no_extras:
         p = packed_varlen(path)
         p["dense_us"] = kern["attn"]["us"] if "attn" in kern else None
         p["note"] = ("AllGather-KV share with the sequence packed as 4 documents: per rank, the remap of "
                      "the packed query boundaries and the packed attention (both timed)")
-        out["packed_varlen"] = p
+        rec["packed_varlen"] = p
     if args.only is None and wl.masked and not args.no_extras:
         j = joint_segments(path)
         j["note"] = ("joint attention over image and text K/V segments (text mask only), "
                      "rear and front layouts, against the concatenated masked call")
-        out["joint_segments"] = j
-    if args.only is None:
-        out["parity"] = parity_sample(path, wl)
-        if not args.no_cpu_baseline:
-            out["cpu_baseline"] = cpu_baseline(wl, path.full, path.mask_np, args.cpu_budget_s)
-    print(json.dumps(out), flush=True)
+        rec["joint_segments"] = j
+    torch.cuda.synchronize()
+    return rec
 
 
 if __name__ == "__main__":

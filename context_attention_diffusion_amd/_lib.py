@@ -25,11 +25,11 @@ SIGNATURES = {
     "cp_unpack_head_sharded": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                               ctypes.c_int, _vp]),
     "cp_attn_localq_globalkv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
-                                               _i64, ctypes.c_float, ctypes.c_int, _vp]),
+                                               _i64, ctypes.c_float, _vp]),
     "cp_output_reverse": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                          ctypes.c_int, _vp]),
     "cp_attn_localq_globalkv_ws": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
-                                                  _i64, ctypes.c_float, ctypes.c_int, _vp,
+                                                  _i64, ctypes.c_float, _vp,
                                                   ctypes.c_size_t, _vp]),
     "cp_attn_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64]),
     "cp_pack_qkv_dst_major_padded": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
@@ -37,20 +37,20 @@ SIGNATURES = {
     "cp_output_merge_cropped": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                                ctypes.c_int, _vp]),
     "cp_attn_joint": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i64, _i64,
-                                     _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, _vp,
+                                     _i64, _i64, _i64, _i64, ctypes.c_float, _vp,
                                      ctypes.c_size_t, _vp]),
     "cp_attn_partial": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
-                                       ctypes.c_float, ctypes.c_int, _vp]),
+                                       ctypes.c_float, _vp]),
     "cp_attn_partial_accum": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
-                                             _i64, ctypes.c_float, ctypes.c_int, _vp]),
+                                             _i64, ctypes.c_float, _vp]),
     "cp_attn_merge": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]),
     "cp_attn_recv_to_send": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
-                                            ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t, _vp]),
+                                            ctypes.c_float, _vp, ctypes.c_size_t, _vp]),
     "cp_varlen_remap_cu_seqlens_q": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp]),
     "cp_attn_varlen": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64,
-                                      ctypes.c_float, ctypes.c_int, _vp]),
+                                      ctypes.c_float, _vp]),
     "cp_attn_recv_to_send_2d": (ctypes.c_int, [_vp, _vp, _vp, _i64, ctypes.c_int, _vp, _vp, _vp, _i64, _i64,
-                                               _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, _vp,
+                                               _i64, _i64, _i64, ctypes.c_float, _vp,
                                                ctypes.c_size_t, _vp]),
 }
 
@@ -70,7 +70,7 @@ CP_ERR_WORKSPACE = 11
 
 CP_DTYPE_BF16 = 0
 CP_DTYPE_FP16 = 1
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 _lib = None
 

@@ -269,6 +269,11 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   __shared__ __attribute__((aligned(1024))) char lds0_v00[C::TILE], lds0_v01[C::TILE], lds0_v10[C::TILE], lds0_v11[C::TILE];
   __shared__ __attribute__((aligned(1024))) char lds1_k00[C::TILE], lds1_k01[C::TILE], lds1_k10[C::TILE], lds1_k11[C::TILE];
   __shared__ __attribute__((aligned(16))) float lds2_bias[6 * C::BN];
+  // Group 1's first K tile, read by its first Q K^T right after the prologue
+  // barrier.  It has a buffer of its own because group 0's first in-loop fills,
+  // issued in the same interval, overwrite group 1's K buffer 0 with its third
+  // tile; nothing orders those writes after that read.
+  __shared__ __attribute__((aligned(1024))) char lds3_k1first[C::TILE];
 
   const int tid = threadIdx.x;
   // Wave-uniform indices go through readfirstlane so that the compiler keeps
@@ -664,7 +669,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       fill(1, 2 * (i0 + 0) + 0, vtile(I0{}, I0{}));
     }
     if (n_g1 > 0) {
-      fill(0, 2 * (i0 + 0) + 1, ktile(I1{}, I0{}));
+      fill(0, 2 * (i0 + 0) + 1, lds3_k1first);
       fill(1, 2 * (i0 + 0) + 1, vtile(I1{}, I0{}));
     }
     if (n_g1 > 1) fill(0, 2 * (i0 + 1) + 1, ktile(I1{}, I1{}));
@@ -735,7 +740,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     }
   } else {
     if (n_g > 0) {
-      qk(ktile(I1{}, I0{}), sc);
+      qk(lds3_k1first, sc);
     }
     auto iter1 = [&](auto par, int i) {
       constexpr int P = decltype(par)::value;
@@ -1232,20 +1237,19 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
 }
 
 // Checks shared by every attention entry point.
-int attn_check(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale, int causal) {
+int attn_check(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale) {
   if (B < 1 || Sq < 1 || Skv < 1 || H < 1) return CP_ERR_SHAPE;
   if (D != 64 && D != 128) return CP_ERR_HEAD_DIM;
   if (!std::isfinite(scale) || !(scale > 0.f)) return CP_ERR_SCALE;
-  if (causal != 0) return CP_ERR_UNSUPPORTED;
   return CP_OK;
 }
 
 // Local-Q / global-KV attention on dense [B][S][H][D] operands.
 int attn_run(const void* q, const void* k, const void* v, const uint8_t* key_mask, void* o, int64_t B,
-             int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale, int causal, void* ws, size_t ws_bytes,
+             int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale, void* ws, size_t ws_bytes,
              cp_stream_t stream) {
   if (!q || !k || !v || !o) return CP_ERR_NULL;
-  if (const int st = attn_check(B, Sq, Skv, H, D, scale, causal)) return st;
+  if (const int st = attn_check(B, Sq, Skv, H, D, scale)) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return CP_ERR_ALIGNMENT;
   if (ws && !aligned16(ws)) return CP_ERR_ALIGNMENT;
   // Per-dimension sizes and the work count are kept in int on the device.
@@ -1272,15 +1276,15 @@ int attn_run(const void* q, const void* k, const void* v, const uint8_t* key_mas
 extern "C" int cp_attn_localq_globalkv(const void* q, const void* k, const void* v,
                                        const uint8_t* key_mask, void* o, int64_t B, int64_t Sq,
                                        int64_t Skv, int64_t H, int64_t D, float scale,
-                                       int causal, cp_stream_t stream) {
-  return attn_run(q, k, v, key_mask, o, B, Sq, Skv, H, D, scale, causal, nullptr, 0, stream);
+                                       cp_stream_t stream) {
+  return attn_run(q, k, v, key_mask, o, B, Sq, Skv, H, D, scale, nullptr, 0, stream);
 }
 
 extern "C" int cp_attn_localq_globalkv_ws(const void* q, const void* k, const void* v,
                                           const uint8_t* key_mask, void* o, int64_t B, int64_t Sq,
-                                          int64_t Skv, int64_t H, int64_t D, float scale, int causal,
+                                          int64_t Skv, int64_t H, int64_t D, float scale,
                                           void* workspace, size_t workspace_bytes, cp_stream_t stream) {
-  return attn_run(q, k, v, key_mask, o, B, Sq, Skv, H, D, scale, causal, workspace, workspace_bytes, stream);
+  return attn_run(q, k, v, key_mask, o, B, Sq, Skv, H, D, scale, workspace, workspace_bytes, stream);
 }
 
 extern "C" int cp_varlen_remap_cu_seqlens_q(const int32_t* cu_q_global, int32_t* cu_q_local, int64_t n_docs,
@@ -1302,10 +1306,10 @@ extern "C" int cp_varlen_remap_cu_seqlens_q(const int32_t* cu_q_global, int32_t*
 
 extern "C" int cp_attn_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                               const int32_t* cu_seqlens_k, int64_t n_docs, void* o,
-                              int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale, int causal,
+                              int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale,
                               cp_stream_t stream) {
   if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return CP_ERR_NULL;
-  if (const int st = attn_check(1, Sq, Skv, H, D, scale, causal)) return st;
+  if (const int st = attn_check(1, Sq, Skv, H, D, scale)) return st;
   constexpr int64_t kIntMax = 0x7fffffff;
   if (n_docs < 1 || n_docs >= kIntMax) return CP_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return CP_ERR_ALIGNMENT;
@@ -1333,14 +1337,14 @@ extern "C" int cp_attn_varlen(const void* q, const void* k, const void* v, const
 extern "C" int cp_attn_joint(const void* q, const void* k_img, const void* v_img, const uint8_t* img_mask,
                              const void* k_joint, const void* v_joint, const uint8_t* joint_mask, int joint_front,
                              void* o, int64_t B, int64_t Sq, int64_t S_img, int64_t T, int64_t H, int64_t D,
-                             float scale, int causal, void* workspace, size_t workspace_bytes, cp_stream_t stream) {
+                             float scale, void* workspace, size_t workspace_bytes, cp_stream_t stream) {
   if (!q || !k_img || !v_img || !o) return CP_ERR_NULL;
   if (T > 0 && (!k_joint || !v_joint)) return CP_ERR_NULL;
   if (T < 0 || S_img < 1) return CP_ERR_SHAPE;
   if (joint_front != 0 && joint_front != 1) return CP_ERR_UNSUPPORTED;
   constexpr int64_t kIntMax = 0x7fffffff;
   if (S_img > kIntMax / 2 || T > kIntMax / 2) return CP_ERR_SHAPE;
-  if (const int st = attn_check(B, Sq, S_img + T, H, D, scale, causal)) return st;
+  if (const int st = attn_check(B, Sq, S_img + T, H, D, scale)) return st;
   if (!aligned16(q) || !aligned16(k_img) || !aligned16(v_img) || !aligned16(o)) return CP_ERR_ALIGNMENT;
   if (T > 0 && (!aligned16(k_joint) || !aligned16(v_joint))) return CP_ERR_ALIGNMENT;
   if (workspace && !aligned16(workspace)) return CP_ERR_ALIGNMENT;
@@ -1377,13 +1381,13 @@ extern "C" int cp_attn_joint(const void* q, const void* k_img, const void* v_img
 
 extern "C" int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, void* send, int64_t B,
                                     int64_t S_local, int64_t H_local, int64_t D, int64_t W, float scale,
-                                    int causal, void* workspace, size_t workspace_bytes, cp_stream_t stream) {
+                                    void* workspace, size_t workspace_bytes, cp_stream_t stream) {
   if (!recv || !send) return CP_ERR_NULL;
   if (W < 1) return CP_ERR_SHAPE;
   constexpr int64_t kIntMax = 0x7fffffff;
   if (S_local < 1 || S_local > kIntMax / W) return CP_ERR_SHAPE;
   const int64_t S = W * S_local;
-  if (const int st = attn_check(B, S, S, H_local, D, scale, causal)) return st;
+  if (const int st = attn_check(B, S, S, H_local, D, scale)) return st;
   if (!aligned16(recv) || !aligned16(send)) return CP_ERR_ALIGNMENT;
   if (workspace && !aligned16(workspace)) return CP_ERR_ALIGNMENT;
   if (B > kIntMax || S > kIntMax - 64 || H_local > kIntMax) return CP_ERR_SHAPE;
@@ -1412,7 +1416,7 @@ extern "C" int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, v
 extern "C" int cp_attn_recv_to_send_2d(const void* recv, const void* k_other, const void* v_other, int64_t S_other,
                                        int other_first, const uint8_t* own_mask, const uint8_t* other_mask,
                                        void* send, int64_t B, int64_t S_local, int64_t H_local, int64_t D,
-                                       int64_t W, float scale, int causal, void* workspace,
+                                       int64_t W, float scale, void* workspace,
                                        size_t workspace_bytes, cp_stream_t stream) {
   if (!recv || !send || !k_other || !v_other) return CP_ERR_NULL;
   if (W < 1 || S_other < 1) return CP_ERR_SHAPE;
@@ -1421,7 +1425,7 @@ extern "C" int cp_attn_recv_to_send_2d(const void* recv, const void* k_other, co
   if (S_local < 1 || S_local > kIntMax / W) return CP_ERR_SHAPE;
   const int64_t S = W * S_local;
   if (S > kIntMax / 2 || S_other > kIntMax / 2) return CP_ERR_SHAPE;
-  if (const int st = attn_check(B, S, S + S_other, H_local, D, scale, causal)) return st;
+  if (const int st = attn_check(B, S, S + S_other, H_local, D, scale)) return st;
   if (!aligned16(recv) || !aligned16(send) || !aligned16(k_other) || !aligned16(v_other)) return CP_ERR_ALIGNMENT;
   if (workspace && !aligned16(workspace)) return CP_ERR_ALIGNMENT;
   if (B > kIntMax || S + S_other > kIntMax - 64 || H_local > kIntMax) return CP_ERR_SHAPE;
@@ -1469,8 +1473,8 @@ namespace {
 // out_o / out_lse: fp32 outputs (may be the state itself); o_final: bf16 output.
 int partial_run(const void* q, const void* k, const void* v, const uint8_t* key_mask, void* out_o,
                 void* out_lse, const void* st_o, const void* st_lse, void* o_final, int64_t B, int64_t Sq,
-                int64_t Skv, int64_t H, int64_t D, float scale, int causal, cp_stream_t stream) {
-  if (const int st = attn_check(B, Sq, Skv, H, D, scale, causal)) return st;
+                int64_t Skv, int64_t H, int64_t D, float scale, cp_stream_t stream) {
+  if (const int st = attn_check(B, Sq, Skv, H, D, scale)) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return CP_ERR_ALIGNMENT;
   if ((out_o && !aligned16(out_o)) || (st_o && !aligned16(st_o)) || (o_final && !aligned16(o_final)))
     return CP_ERR_ALIGNMENT;
@@ -1511,22 +1515,22 @@ int partial_run(const void* q, const void* k, const void* v, const uint8_t* key_
 
 extern "C" int cp_attn_partial(const void* q, const void* k, const void* v, const uint8_t* key_mask,
                                void* o_part, void* lse, int64_t B, int64_t Sq, int64_t Skv, int64_t H,
-                               int64_t D, float scale, int causal, cp_stream_t stream) {
+                               int64_t D, float scale, cp_stream_t stream) {
   if (!q || !k || !v || !o_part || !lse) return CP_ERR_NULL;
-  return partial_run(q, k, v, key_mask, o_part, lse, nullptr, nullptr, nullptr, B, Sq, Skv, H, D, scale, causal,
+  return partial_run(q, k, v, key_mask, o_part, lse, nullptr, nullptr, nullptr, B, Sq, Skv, H, D, scale,
                      stream);
 }
 
 extern "C" int cp_attn_partial_accum(const void* q, const void* k, const void* v, const uint8_t* key_mask,
                                      void* state_o, void* state_lse, void* o_final, int64_t B, int64_t Sq,
-                                     int64_t Skv, int64_t H, int64_t D, float scale, int causal,
+                                     int64_t Skv, int64_t H, int64_t D, float scale,
                                      cp_stream_t stream) {
   if (!q || !k || !v || !state_o || !state_lse) return CP_ERR_NULL;
   if (o_final)
     return partial_run(q, k, v, key_mask, nullptr, nullptr, state_o, state_lse, o_final, B, Sq, Skv, H, D, scale,
-                       causal, stream);
+                       stream);
   return partial_run(q, k, v, key_mask, state_o, state_lse, state_o, state_lse, nullptr, B, Sq, Skv, H, D, scale,
-                     causal, stream);
+                     stream);
 }
 
 extern "C" int cp_attn_merge(const void* o_parts, const void* lses, int64_t N, void* o, int64_t B, int64_t Sq,

@@ -165,7 +165,7 @@ def cp_unpack_head_sharded(recv, B: int, W: int, out=None, stream=None):
     return out
 
 
-def cp_attn_localq_globalkv(q, k, v, key_mask=None, scale=None, out=None, causal=False,
+def cp_attn_localq_globalkv(q, k, v, key_mask=None, scale=None, out=None,
                             stream=None, split=True, workspace=None) -> torch.Tensor:
     """Non-causal attention: q [B,Sq,H,D] vs k, v [B,Skv,H,D] (bf16), optional uint8 mask [B,Skv].
 
@@ -196,7 +196,7 @@ def cp_attn_localq_globalkv(q, k, v, key_mask=None, scale=None, out=None, causal
     if not split:
         _lib.check("cp_attn_localq_globalkv", lib.cp_attn_localq_globalkv(
             _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), mask_ptr, _dev(out, "o"),
-            B, Sq, Skv, H, D, float(scale), int(bool(causal)), _stream(stream)))
+            B, Sq, Skv, H, D, float(scale), _stream(stream)))
         return out
     need = int(lib.cp_attn_workspace_bytes(B, Sq, Skv, H, D))
     if workspace is None:
@@ -205,13 +205,13 @@ def cp_attn_localq_globalkv(q, k, v, key_mask=None, scale=None, out=None, causal
         raise ValueError("workspace must be a 1-D uint8 tensor")
     _lib.check("cp_attn_localq_globalkv_ws", lib.cp_attn_localq_globalkv_ws(
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), mask_ptr, _dev(out, "o"),
-        B, Sq, Skv, H, D, float(scale), int(bool(causal)), _dev(workspace, "workspace"),
+        B, Sq, Skv, H, D, float(scale), _dev(workspace, "workspace"),
         workspace.numel(), _stream(stream)))
     return out
 
 
 def cp_attn_joint(q, k_img, v_img, k_joint=None, v_joint=None, img_mask=None, joint_mask=None,
-                  joint_front=False, scale=None, out=None, causal=False, stream=None, split=True,
+                  joint_front=False, scale=None, out=None, stream=None, split=True,
                   workspace=None) -> torch.Tensor:
     """Attention of q [B,Sq,H,D] over two key segments, image [B,S_img,H,D] and joint
     [B,T,H,D] (None: T = 0), in the order joint_front selects, with per-segment uint8
@@ -252,12 +252,12 @@ def cp_attn_joint(q, k_img, v_img, k_joint=None, v_joint=None, img_mask=None, jo
     _lib.check("cp_attn_joint", lib.cp_attn_joint(
         _dev(q, "q"), _dev(k_img, "k_img"), _dev(v_img, "v_img"), im,
         _dev(k_joint, "k_joint") if T else None, _dev(v_joint, "v_joint") if T else None, jm,
-        int(bool(joint_front)), _dev(out, "o"), B, Sq, S_img, T, H, D, float(scale), int(bool(causal)),
+        int(bool(joint_front)), _dev(out, "o"), B, Sq, S_img, T, H, D, float(scale),
         ws_ptr, ws_bytes, _stream(stream)))
     return out
 
 
-def cp_attn_partial(q, k, v, key_mask=None, scale=None, out=None, lse=None, causal=False,
+def cp_attn_partial(q, k, v, key_mask=None, scale=None, out=None, lse=None,
                     stream=None):
     """Attention over one K/V chunk: (o_part fp32 [B,Sq,H,D], lse fp32 [B,H,Sq], natural log).
 
@@ -286,12 +286,12 @@ def cp_attn_partial(q, k, v, key_mask=None, scale=None, out=None, lse=None, caus
         raise ValueError("lse must be float32 [B, H, Sq]")
     _lib.check("cp_attn_partial", lib.cp_attn_partial(
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), mask_ptr, _dev(out, "o_part"), _dev(lse, "lse"),
-        B, Sq, Skv, H, D, float(scale), int(bool(causal)), _stream(stream)))
+        B, Sq, Skv, H, D, float(scale), _stream(stream)))
     return out, lse
 
 
 def cp_attn_partial_accum(q, k, v, state_o, state_lse, key_mask=None, scale=None, final=False, out=None,
-                          causal=False, stream=None):
+                          stream=None):
     """Fold attention over one more K/V chunk into a running state (fp32 state_o [B,Sq,H,D],
     state_lse [B,H,Sq], as cp_attn_partial writes them).  final=False updates the state in
     place and returns (state_o, state_lse); final=True returns the merged bf16 output."""
@@ -322,7 +322,7 @@ def cp_attn_partial_accum(q, k, v, state_o, state_lse, key_mask=None, scale=None
         o_ptr = _dev(out, "o_final")
     _lib.check("cp_attn_partial_accum", lib.cp_attn_partial_accum(
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), mask_ptr, _dev(state_o, "state_o"),
-        _dev(state_lse, "state_lse"), o_ptr, B, Sq, Skv, H, D, float(scale), int(bool(causal)),
+        _dev(state_lse, "state_lse"), o_ptr, B, Sq, Skv, H, D, float(scale),
         _stream(stream)))
     return out if final else (state_o, state_lse)
 
@@ -342,7 +342,7 @@ def cp_attn_merge(o_parts, lses, out=None, stream=None) -> torch.Tensor:
     return out
 
 
-def cp_attn_recv_to_send(recv, B: int, W: int, key_mask=None, scale=None, out=None, causal=False,
+def cp_attn_recv_to_send(recv, B: int, W: int, key_mask=None, scale=None, out=None,
                          stream=None, split=True, workspace=None) -> torch.Tensor:
     """Ulysses attention straight from the received staging buffer into the send layout.
 
@@ -381,12 +381,12 @@ def cp_attn_recv_to_send(recv, B: int, W: int, key_mask=None, scale=None, out=No
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel()
     _lib.check("cp_attn_recv_to_send", lib.cp_attn_recv_to_send(
         _dev(recv, "recv"), mask_ptr, _dev(out, "send"), B, Sl, Hl, D, W, float(scale),
-        int(bool(causal)), ws_ptr, ws_bytes, _stream(stream)))
+        ws_ptr, ws_bytes, _stream(stream)))
     return out
 
 
 def cp_attn_recv_to_send_2d(recv, k_other, v_other, B: int, W: int, other_first: bool = False,
-                            own_mask=None, other_mask=None, scale=None, out=None, causal=False,
+                            own_mask=None, other_mask=None, scale=None, out=None,
                             stream=None, split=True, workspace=None) -> torch.Tensor:
     """2D-layout Ulysses attention from the received staging buffer into the send layout.
 
@@ -437,7 +437,7 @@ def cp_attn_recv_to_send_2d(recv, k_other, v_other, B: int, W: int, other_first:
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel()
     _lib.check("cp_attn_recv_to_send_2d", lib.cp_attn_recv_to_send_2d(
         _dev(recv, "recv"), _dev(k_other, "k_other"), _dev(v_other, "v_other"), So, int(bool(other_first)),
-        om, xm, _dev(out, "send"), B, Sl, Hl, D, W, float(scale), int(bool(causal)), ws_ptr, ws_bytes,
+        om, xm, _dev(out, "send"), B, Sl, Hl, D, W, float(scale), ws_ptr, ws_bytes,
         _stream(stream)))
     return out
 
@@ -460,7 +460,7 @@ def cp_varlen_remap_cu_seqlens_q(cu_q_global, rank: int, S_local: int, out=None,
 
 
 def cp_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, out=None,
-                   causal=False, stream=None) -> torch.Tensor:
+                   stream=None) -> torch.Tensor:
     """Packed variable-length attention: q [Sq, H, D], k / v [Skv, H, D] bf16; query
     document i (rows cu_seqlens_q[i]..cu_seqlens_q[i+1]) attends to key document i
     only.  The boundary arrays are int32 device tensors of n_docs + 1 entries.
@@ -486,7 +486,7 @@ def cp_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, out=None,
     _lib.check("cp_attn_varlen", lib.cp_attn_varlen(
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(cu_seqlens_q, "cu_seqlens_q"),
         _dev(cu_seqlens_k, "cu_seqlens_k"), cu_seqlens_q.numel() - 1, _dev(out, "o"),
-        Sq, k.shape[0], H, D, float(scale), int(bool(causal)), _stream(stream)))
+        Sq, k.shape[0], H, D, float(scale), _stream(stream)))
     return out
 
 

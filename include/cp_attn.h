@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CP_ABI_VERSION 9
+#define CP_ABI_VERSION 10
 
 typedef struct ihipStream_t* cp_stream_t; /* == hipStream_t */
 
@@ -68,7 +68,7 @@ enum cp_status {
   CP_ERR_ALIGNMENT = 6,    /* a pointer is not 16-byte aligned */
   CP_ERR_ALIAS = 7,        /* an output overlaps an input or another output */
   CP_ERR_SCALE = 8,        /* softmax scale is not finite or not > 0 */
-  CP_ERR_UNSUPPORTED = 9,  /* a valid but unsupported request (causal, bad phase, W too large) */
+  CP_ERR_UNSUPPORTED = 9,  /* a valid but unsupported request (bad phase or layout flag, W too large) */
   CP_ERR_HIP = 10,         /* the HIP runtime rejected the launch */
   CP_ERR_WORKSPACE = 11    /* the workspace is too small (see cp_attn_workspace_bytes) */
 };
@@ -176,7 +176,10 @@ int cp_unpack_head_sharded(const void* recv, void* q_out, void* k_out, void* v_o
  *   key_mask : NULL, or [B][Skv] uint8 key-validity mask, nonzero = attend (the
  *              2D key mask of [vllm-omni#7641]'s review fixes; any alignment)
  *   scale    : softmax scale, finite and > 0 (1/sqrt(D) for standard attention)
- *   causal   : must be 0 (causal attention is rejected, as in [vllm-omni#7641])
+ *
+ * Non-causal is the only mode: the pages attend every query to every valid key
+ * ([chitu-fastcp] "Support scope" lists non-causal attention only), so there is
+ * no causal flag.
  *
  * Softmax statistics and accumulation are fp32; probabilities are rounded to
  * bf16 before the P.V product; o is rounded to nearest-even bf16.  A query row
@@ -186,7 +189,7 @@ int cp_unpack_head_sharded(const void* recv, void* q_out, void* k_out, void* v_o
 int cp_attn_localq_globalkv(const void* q, const void* k, const void* v,
                             const uint8_t* key_mask, void* o,
                             int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D,
-                            float scale, int causal, cp_stream_t stream);
+                            float scale, cp_stream_t stream);
 
 /*
  * The same attention with a caller-owned workspace, which lets the library
@@ -211,7 +214,7 @@ int cp_attn_localq_globalkv(const void* q, const void* k, const void* v,
 int cp_attn_localq_globalkv_ws(const void* q, const void* k, const void* v,
                                const uint8_t* key_mask, void* o,
                                int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D,
-                               float scale, int causal, void* workspace, size_t workspace_bytes,
+                               float scale, void* workspace, size_t workspace_bytes,
                                cp_stream_t stream);
 
 /*
@@ -248,7 +251,7 @@ size_t cp_attn_workspace_bytes(int64_t B, int64_t Sq, int64_t Skv, int64_t H, in
 int cp_attn_joint(const void* q, const void* k_img, const void* v_img, const uint8_t* img_mask,
                   const void* k_joint, const void* v_joint, const uint8_t* joint_mask, int joint_front,
                   void* o, int64_t B, int64_t Sq, int64_t S_img, int64_t T, int64_t H, int64_t D,
-                  float scale, int causal, void* workspace, size_t workspace_bytes, cp_stream_t stream);
+                  float scale, void* workspace, size_t workspace_bytes, cp_stream_t stream);
 
 /*
  * Attention over keys that arrive in chunks: a forward pass over one K/V chunk
@@ -271,7 +274,7 @@ int cp_attn_joint(const void* q, const void* k_img, const void* v_img, const uin
  */
 int cp_attn_partial(const void* q, const void* k, const void* v, const uint8_t* key_mask,
                     void* o_part, void* lse, int64_t B, int64_t Sq, int64_t Skv, int64_t H,
-                    int64_t D, float scale, int causal, cp_stream_t stream);
+                    int64_t D, float scale, cp_stream_t stream);
 
 /*
  * Attention over the next key chunk folded into a running state, for K/V that
@@ -295,7 +298,7 @@ int cp_attn_partial(const void* q, const void* k, const void* v, const uint8_t* 
  */
 int cp_attn_partial_accum(const void* q, const void* k, const void* v, const uint8_t* key_mask,
                           void* state_o, void* state_lse, void* o_final, int64_t B, int64_t Sq, int64_t Skv,
-                          int64_t H, int64_t D, float scale, int causal, cp_stream_t stream);
+                          int64_t H, int64_t D, float scale, cp_stream_t stream);
 
 /*
  * Merge of N partial results of the same queries over disjoint key sets:
@@ -333,7 +336,7 @@ int cp_attn_merge(const void* o_parts, const void* lses, int64_t N, void* o,
  *   workspace : as for cp_attn_localq_globalkv_ws (sized by
  *               cp_attn_workspace_bytes(B, S, S, H_local, D)), or NULL
  *
- * Requires the attention's conditions (D in {64, 128}, scale, causal == 0),
+ * Requires the attention's conditions (D in {64, 128}, scale),
  * W >= 1, 16-byte aligned pointers, send disjoint from recv and key_mask.  With
  * B > 1 a batch's rows arrive in W chunks of S_local rows; when S_local is not a
  * multiple of 64, key tiles that span chunks are addressed row by row, which
@@ -341,7 +344,7 @@ int cp_attn_merge(const void* o_parts, const void* lses, int64_t N, void* o,
  */
 int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, void* send,
                          int64_t B, int64_t S_local, int64_t H_local, int64_t D, int64_t W,
-                         float scale, int causal, void* workspace, size_t workspace_bytes,
+                         float scale, void* workspace, size_t workspace_bytes,
                          cp_stream_t stream);
 
 /*
@@ -375,7 +378,7 @@ int cp_attn_recv_to_send(const void* recv, const uint8_t* key_mask, void* send,
 int cp_attn_recv_to_send_2d(const void* recv, const void* k_other, const void* v_other, int64_t S_other,
                             int other_first, const uint8_t* own_mask, const uint8_t* other_mask,
                             void* send, int64_t B, int64_t S_local, int64_t H_local, int64_t D,
-                            int64_t W, float scale, int causal, void* workspace, size_t workspace_bytes,
+                            int64_t W, float scale, void* workspace, size_t workspace_bytes,
                             cp_stream_t stream);
 
 /*
@@ -442,12 +445,12 @@ int cp_varlen_remap_cu_seqlens_q(const int32_t* cu_q_global, int32_t* cu_q_local
  * earlier document has rows there too; no max_seqlen_q is needed.  A document with query rows and no key
  * rows gets zero outputs.  Rows of o outside every document are not written (the
  * one exception to "outputs are fully overwritten").  No key mask, no split; D in
- * {64, 128}, causal == 0, 16-byte aligned q, k, v, o and 4-byte aligned boundary
+ * {64, 128}, 16-byte aligned q, k, v, o and 4-byte aligned boundary
  * arrays; n_docs >= 1.
  */
 int cp_attn_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                    const int32_t* cu_seqlens_k, int64_t n_docs, void* o,
-                   int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale, int causal,
+                   int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale,
                    cp_stream_t stream);
 
 #ifdef __cplusplus

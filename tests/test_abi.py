@@ -96,45 +96,44 @@ def _unpack(**kw):
 
 def _attn(**kw):
     a = dict(q=A, k=A + BIG, v=A + 2 * BIG, m=None, o=A + 3 * BIG, B=1, Sq=8, Skv=16, H=2,
-             D=128, scale=0.125, causal=0)
+             D=128, scale=0.125)
     a.update(kw)
     return _lib.load().cp_attn_localq_globalkv(a["q"], a["k"], a["v"], a["m"], a["o"], a["B"],
-                                               a["Sq"], a["Skv"], a["H"], a["D"], a["scale"],
-                                               a["causal"], None)
+                                               a["Sq"], a["Skv"], a["H"], a["D"], a["scale"], None)
 
 
 def _attn_ws(**kw):
     a = dict(q=A, k=A + BIG, v=A + 2 * BIG, m=None, o=A + 3 * BIG, B=1, Sq=8, Skv=16, H=2,
-             D=128, scale=0.125, causal=0, ws=A + 5 * BIG, nbytes=16)
+             D=128, scale=0.125, ws=A + 5 * BIG, nbytes=16)
     a.update(kw)
     return _lib.load().cp_attn_localq_globalkv_ws(a["q"], a["k"], a["v"], a["m"], a["o"], a["B"],
                                                   a["Sq"], a["Skv"], a["H"], a["D"], a["scale"],
-                                                  a["causal"], a["ws"], a["nbytes"], None)
+                                                  a["ws"], a["nbytes"], None)
 
 
 def _fused(**kw):
-    a = dict(r=A, m=None, s=A + BIG, B=1, Sl=128, Hl=2, D=128, W=2, scale=0.125, causal=0,
+    a = dict(r=A, m=None, s=A + BIG, B=1, Sl=128, Hl=2, D=128, W=2, scale=0.125,
              ws=None, nbytes=0)
     a.update(kw)
     return _lib.load().cp_attn_recv_to_send(a["r"], a["m"], a["s"], a["B"], a["Sl"], a["Hl"], a["D"],
-                                            a["W"], a["scale"], a["causal"], a["ws"], a["nbytes"], None)
+                                            a["W"], a["scale"], a["ws"], a["nbytes"], None)
 
 
 def _fused2d(**kw):
     a = dict(r=A, ko=A + 2 * BIG, vo=A + 3 * BIG, So=256, first=0, om=None, xm=None, s=A + BIG, B=1, Sl=128,
-             Hl=2, D=128, W=2, scale=0.125, causal=0, ws=None, nbytes=0)
+             Hl=2, D=128, W=2, scale=0.125, ws=None, nbytes=0)
     a.update(kw)
     return _lib.load().cp_attn_recv_to_send_2d(a["r"], a["ko"], a["vo"], a["So"], a["first"], a["om"], a["xm"],
                                                a["s"], a["B"], a["Sl"], a["Hl"], a["D"], a["W"], a["scale"],
-                                               a["causal"], a["ws"], a["nbytes"], None)
+                                               a["ws"], a["nbytes"], None)
 
 
 def _varlen(**kw):
     a = dict(q=A, k=A + BIG, v=A + 2 * BIG, cq=A + 3 * BIG, ck=A + 4 * BIG, n=2, o=A + 5 * BIG, Sq=100,
-             Skv=200, H=2, D=128, scale=0.125, causal=0)
+             Skv=200, H=2, D=128, scale=0.125)
     a.update(kw)
     return _lib.load().cp_attn_varlen(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["n"], a["o"], a["Sq"],
-                                      a["Skv"], a["H"], a["D"], a["scale"], a["causal"], None)
+                                      a["Skv"], a["H"], a["D"], a["scale"], None)
 
 
 def _remap(**kw):
@@ -145,18 +144,18 @@ def _remap(**kw):
 
 def _partial(**kw):
     a = dict(q=A, k=A + BIG, v=A + 2 * BIG, m=None, o=A + 3 * BIG, lse=A + 4 * BIG, B=1, Sq=8, Skv=16,
-             H=2, D=128, scale=0.125, causal=0)
+             H=2, D=128, scale=0.125)
     a.update(kw)
     return _lib.load().cp_attn_partial(a["q"], a["k"], a["v"], a["m"], a["o"], a["lse"], a["B"], a["Sq"],
-                                       a["Skv"], a["H"], a["D"], a["scale"], a["causal"], None)
+                                       a["Skv"], a["H"], a["D"], a["scale"], None)
 
 
 def _accum(**kw):
     a = dict(q=A, k=A + BIG, v=A + 2 * BIG, m=None, so=A + 3 * BIG, sl=A + 4 * BIG, of=None, B=1, Sq=8,
-             Skv=16, H=2, D=128, scale=0.125, causal=0)
+             Skv=16, H=2, D=128, scale=0.125)
     a.update(kw)
     return _lib.load().cp_attn_partial_accum(a["q"], a["k"], a["v"], a["m"], a["so"], a["sl"], a["of"], a["B"],
-                                             a["Sq"], a["Skv"], a["H"], a["D"], a["scale"], a["causal"], None)
+                                             a["Sq"], a["Skv"], a["H"], a["D"], a["scale"], None)
 
 
 def _merge(**kw):
@@ -167,11 +166,11 @@ def _merge(**kw):
 
 def _joint(**kw):
     a = dict(q=A, ki=A + BIG, vi=A + 2 * BIG, im=None, kj=A + 3 * BIG, vj=A + 4 * BIG, jm=None, front=0,
-             o=A + 5 * BIG, B=1, Sq=8, Si=64, T=16, H=2, D=128, scale=0.125, causal=0, ws=None, nbytes=0)
+             o=A + 5 * BIG, B=1, Sq=8, Si=64, T=16, H=2, D=128, scale=0.125, ws=None, nbytes=0)
     a.update(kw)
     return _lib.load().cp_attn_joint(a["q"], a["ki"], a["vi"], a["im"], a["kj"], a["vj"], a["jm"], a["front"],
                                      a["o"], a["B"], a["Sq"], a["Si"], a["T"], a["H"], a["D"], a["scale"],
-                                     a["causal"], a["ws"], a["nbytes"], None)
+                                     a["ws"], a["nbytes"], None)
 
 
 def _rev(**kw):
@@ -235,7 +234,6 @@ def test_unpack_rejects(kw, code):
     (dict(scale=-1.0), _lib.CP_ERR_SCALE),
     (dict(scale=math.nan), _lib.CP_ERR_SCALE),
     (dict(scale=math.inf), _lib.CP_ERR_SCALE),
-    (dict(causal=1), _lib.CP_ERR_UNSUPPORTED),
     (dict(v=A + 2 * BIG + 8), _lib.CP_ERR_ALIGNMENT),
     (dict(o=A + 16), _lib.CP_ERR_ALIAS),             # o overlaps q
     (dict(o=A + BIG + 16), _lib.CP_ERR_ALIAS),       # o overlaps k
@@ -253,7 +251,6 @@ def test_attention_rejects(kw, code):
     (dict(Skv=4096, ws=A + 3 * BIG, nbytes=1 << 30), _lib.CP_ERR_ALIAS),   # workspace overlaps o
     (dict(o=None), _lib.CP_ERR_NULL),
     (dict(D=96), _lib.CP_ERR_HEAD_DIM),
-    (dict(causal=1), _lib.CP_ERR_UNSUPPORTED),
 ])
 def test_attention_ws_rejects(kw, code):
     assert _attn_ws(**kw) == code
@@ -268,7 +265,6 @@ def test_attention_ws_rejects(kw, code):
     (dict(B=0), _lib.CP_ERR_SHAPE),
     (dict(D=96), _lib.CP_ERR_HEAD_DIM),
     (dict(scale=0.0), _lib.CP_ERR_SCALE),
-    (dict(causal=1), _lib.CP_ERR_UNSUPPORTED),
     (dict(r=A + 8), _lib.CP_ERR_ALIGNMENT),
     (dict(ws=A + 5 * BIG + 8, nbytes=1 << 20), _lib.CP_ERR_ALIGNMENT),
     (dict(s=A + 4096), _lib.CP_ERR_ALIAS),                      # send overlaps recv
@@ -294,7 +290,6 @@ def test_recv_to_send_rejects(kw, code):
     (dict(first=2), _lib.CP_ERR_UNSUPPORTED),
     (dict(D=96), _lib.CP_ERR_HEAD_DIM),
     (dict(scale=0.0), _lib.CP_ERR_SCALE),
-    (dict(causal=1), _lib.CP_ERR_UNSUPPORTED),
     (dict(ko=A + 2 * BIG + 8), _lib.CP_ERR_ALIGNMENT),
     (dict(s=A + 4096), _lib.CP_ERR_ALIAS),                      # send overlaps recv
     (dict(s=A + 2 * BIG + 64), _lib.CP_ERR_ALIAS),              # send overlaps k_other
@@ -318,7 +313,6 @@ def test_recv_to_send_2d_rejects(kw, code):
     (dict(H=1 << 24), _lib.CP_ERR_SHAPE),             # a K/V tile's rows beyond 32-bit offsets
     (dict(D=96), _lib.CP_ERR_HEAD_DIM),
     (dict(scale=0.0), _lib.CP_ERR_SCALE),
-    (dict(causal=1), _lib.CP_ERR_UNSUPPORTED),
     (dict(o=A + 5 * BIG + 8), _lib.CP_ERR_ALIGNMENT),
     (dict(cq=A + 3 * BIG + 2), _lib.CP_ERR_ALIGNMENT),
     (dict(o=A + 64), _lib.CP_ERR_ALIAS),              # o over q
@@ -351,7 +345,6 @@ def test_remap_rejects(kw, code):
     (dict(Skv=0), _lib.CP_ERR_SHAPE),
     (dict(D=96), _lib.CP_ERR_HEAD_DIM),
     (dict(scale=-1.0), _lib.CP_ERR_SCALE),
-    (dict(causal=1), _lib.CP_ERR_UNSUPPORTED),
     (dict(o=A + 3 * BIG + 8), _lib.CP_ERR_ALIGNMENT),
     (dict(lse=A + 4 * BIG + 2), _lib.CP_ERR_ALIGNMENT),
     (dict(o=A + 16), _lib.CP_ERR_ALIAS),              # o_part overlaps q
@@ -431,7 +424,6 @@ def test_merge_cropped_rejects(kw, code):
     (dict(Si=0), _lib.CP_ERR_SHAPE),
     (dict(front=2), _lib.CP_ERR_UNSUPPORTED),
     (dict(D=96), _lib.CP_ERR_HEAD_DIM),
-    (dict(causal=1), _lib.CP_ERR_UNSUPPORTED),
     (dict(vj=A + 4 * BIG + 8), _lib.CP_ERR_ALIGNMENT),
     (dict(o=A + 3 * BIG + 32), _lib.CP_ERR_ALIAS),  # o overlaps k_joint
     (dict(jm=A + 5 * BIG + 8), _lib.CP_ERR_ALIAS),  # joint mask inside o

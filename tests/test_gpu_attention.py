@@ -1,9 +1,9 @@
 """GPU parity of cp_attn_localq_globalkv against the fp64 oracle.
 
 Bar: max|err| <= 2e-2 and mean|err| <= 2e-3 against the fp64 oracle on the same
-bf16 inputs.  Small and ragged shapes are compared element by element over the
-whole output; the full-size workloads are compared on sampled output rows that
-the oracle computes one by one, plus properties that hold at any size.
+bf16 inputs.  Every test compares the whole output element by element: small and ragged
+shapes, and the full-size workloads (whose oracle results are computed once per
+process, tests/oracle_ref.py), plus properties that hold at any size.
 """
 
 import math
@@ -140,29 +140,19 @@ def test_deterministic(gu):
     np.testing.assert_array_equal(a, b)
 
 
-def _sample_rows(wl, n, seed):
-    rng = np.random.default_rng(seed)
-    rows = {(0, 0, 0), (wl.B - 1, wl.attn_rows - 1, wl.attn_heads - 1),
-            (0, wl.attn_rows - 1, 0), (wl.B - 1, 0, wl.attn_heads - 1)}
-    while len(rows) < n:
-        rows.add((int(rng.integers(wl.B)), int(rng.integers(wl.attn_rows)),
-                  int(rng.integers(wl.attn_heads))))
-    return sorted(rows)
-
-
 @pytest.mark.parametrize("name", ["image_cp4", "image_cp8", "video_u2a2", "joint_cfg_cp4"])
-def test_full_size_workloads_sampled(gu, name):
+def test_full_size_workloads_whole(gu, name):
+    """Rank 0's attention at the workload's full size, every output element against
+    the fp64 oracle."""
+    from oracle_ref import workload_attention
     wl = workloads.WORKLOADS[name]
     print(f"[attn] full-size {name}", flush=True)
     qg, kg, vg = workloads.global_qkv(wl, heads=wl.attn_heads)
     q = np.ascontiguousarray(qg[:, :wl.attn_rows])
     mask = workloads.key_mask(wl)
     got = _run(gu, q, kg, vg, mask, scale=1.0 / math.sqrt(wl.D))
-    rows = _sample_rows(wl, 48, wl.seed)
-    ref = OA.attention_rows(bf16.bits_to_f64(q), bf16.bits_to_f64(kg), bf16.bits_to_f64(vg),
-                            rows, mask, scale=1.0 / math.sqrt(wl.D))
-    sel = np.stack([got[b, i, h] for (b, i, h) in rows])
-    _assert_close(sel, ref, f"{name} sampled rows")
+    ref = workload_attention(name, 0, wl.attn_rows, wl.attn_heads)
+    _assert_close(got, ref, f"{name} whole output")
     # Any-size property: every output lies within [min, max] of the valid value rows.
     vf = torch.from_numpy(vg).view(torch.int16).view(torch.bfloat16).float()
     for b in range(wl.B):
@@ -197,15 +187,8 @@ def test_split_kv_matches_oracle_and_unsplit(gu, B, H, Sq, Skv, D, masked):
     torch.cuda.synchronize()
     assert torch.equal(o_split, o_split2), "split results differ between runs"
     got, whole = gu.to_f64(o_split), gu.to_f64(o_whole)
-    if Sq * Skv * H * B <= 4_000_000:
-        ref = OA.attention(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), mask)
-        _assert_close(got, ref, f"split B{B} H{H} Sq{Sq} Skv{Skv} D{D} m{int(masked)}")
-    else:  # sampled rows at full size
-        rng = np.random.default_rng(seed)
-        rows = [(int(rng.integers(B)), int(rng.integers(Sq)), int(rng.integers(H))) for _ in range(48)]
-        ref = OA.attention_rows(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), rows, mask)
-        sel = np.stack([got[b_, i_, h_] for b_, i_, h_ in rows])
-        _assert_close(sel, ref, f"split sampled B{B} H{H} Sq{Sq} Skv{Skv}")
+    ref = OA.attention(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), mask)
+    _assert_close(got, ref, f"split B{B} H{H} Sq{Sq} Skv{Skv} D{D} m{int(masked)}")
     # the two schedules sum the same terms in a different order
     assert np.abs(got - whole).max() <= 2e-2
 
@@ -293,11 +276,12 @@ def test_recv_to_send_2d_matches_oracle_and_unfused(gu, B, W, Sl, Hl, D, So, oth
 
 
 @pytest.mark.parametrize("name", ["image_cp4", "joint_cfg_cp4"])
-def test_recv_to_send_full_size_sampled(gu, name):
-    """Rank 0 of the workload's Ulysses group at full size: sampled rows against the
-    oracle, the whole output against the unfused chain."""
+def test_recv_to_send_full_size_whole(gu, name):
+    """Rank 0 of the workload's Ulysses group at full size: the whole send buffer
+    against the unfused chain (bit for bit) and against the oracle (every element)."""
     import context_attention_diffusion_amd as cp
     from oracle import layout as OL
+    from oracle_ref import workload_attention
     wl = workloads.WORKLOADS[name]
     W, B, Sl, D = wl.W, wl.B, wl.S_local, wl.D
     Hl = wl.H // W
@@ -312,25 +296,22 @@ def test_recv_to_send_full_size_sampled(gu, name):
     ref_gpu = _fused_ref_chain(cp, rd, B, W, md)
     torch.cuda.synchronize()
     assert torch.equal(got, ref_gpu)
-    # rank 0 holds heads [0, Hl) of the sequence-concatenated global tensors
-    q, k, v = (bf16.bits_to_f64(np.ascontiguousarray(t[:, :, :Hl])) for t in full)
-    rng = np.random.default_rng(wl.seed + 5)
-    S = W * Sl
-    rows = [(int(rng.integers(B)), int(rng.integers(S)), int(rng.integers(Hl))) for _ in range(32)]
-    ref = OA.attention_rows(q, k, v, rows, mask, 1.0 / math.sqrt(D))
-    g = gu.to_f64(got)
-    sel = np.stack([g[i // Sl, b, i % Sl, h] for b, i, h in rows])
-    _assert_close(sel, ref, f"recv_to_send {name} sampled")
+    # rank 0 holds heads [0, Hl) of the sequence-concatenated global tensors; the send
+    # layout [W][B][S_l][Hl][D] puts global row r*S_l + s of batch b at [r, b, s]
+    ref = workload_attention(name, 0, W * Sl, Hl)
+    g = gu.to_f64(got).transpose(1, 0, 2, 3, 4).reshape(B, W * Sl, Hl, D)
+    _assert_close(g, ref, f"recv_to_send {name} whole output")
 
 
 @pytest.mark.parametrize("a", [0, 1])
-def test_recv_to_send_2d_full_size_sampled(gu, a):
+def test_recv_to_send_2d_full_size_whole(gu, a):
     """The video 2D layout (U 2 x A 2) at full size, Ulysses rank u = 0 of AllGather
     index a: the received buffer of its Ulysses group and the other AllGather rank's
-    resident K/V of the same heads; the whole send buffer against the unfused chain,
-    sampled rows against the oracle."""
+    resident K/V of the same heads; the whole send buffer against the unfused chain
+    (bit for bit) and against the oracle (every element)."""
     import context_attention_diffusion_amd as cp
     from oracle import layout as OL
+    from oracle_ref import workload_attention
     wl = workloads.WORKLOADS["video_u2a2"]
     U, A, Sl, D = wl.W, wl.A, wl.S_local, wl.D
     Hl = wl.H // U
@@ -341,6 +322,7 @@ def test_recv_to_send_2d_full_size_sampled(gu, a):
     recv0 = OL.exchange([OL.pack_qkv_dst_major(*shards[r], U) for r in range(U)])[0]
     o_reg = slice((1 - a) * reg, (2 - a) * reg)
     ko, vo = (np.ascontiguousarray(t[:, o_reg, :Hl]) for t in full[1:])
+    del full, shards
     rd, kd, vd = gu.to_dev(recv0), gu.to_dev(ko), gu.to_dev(vo)
     print(f"[attn] recv_to_send_2d full video_u2a2 a={a}", flush=True)
     got = cp.cp_attn_recv_to_send_2d(rd, kd, vd, 1, U, other_first=(a == 1))
@@ -350,13 +332,9 @@ def test_recv_to_send_2d_full_size_sampled(gu, a):
     torch.cuda.synchronize()
     assert torch.equal(got, ref_gpu)
     # rank (a, 0): query rows of region a, heads [0, Hl), against every key row of those heads
-    qf, kf, vf = (bf16.bits_to_f64(np.ascontiguousarray(t[:, :, :Hl])) for t in full)
-    rng = np.random.default_rng(wl.seed + 11 + a)
-    rows = [(0, int(rng.integers(reg)), int(rng.integers(Hl))) for _ in range(24)]
-    ref = OA.attention_rows(qf[:, a * reg:(a + 1) * reg], kf, vf, rows, None, 1.0 / math.sqrt(D))
-    g = gu.to_f64(got)
-    sel = np.stack([g[i // Sl, 0, i % Sl, h] for _, i, h in rows])
-    _assert_close(sel, ref, f"recv_to_send_2d video a={a} sampled")
+    ref = workload_attention("video_u2a2", a * reg, (a + 1) * reg, Hl)
+    g = gu.to_f64(got).reshape(1, reg, Hl, D)      # B == 1: the send layout is the row order
+    _assert_close(g, ref, f"recv_to_send_2d video a={a} whole output")
 
 
 # ------------------------------------------ attention over K/V chunks, then merge
@@ -417,9 +395,11 @@ def test_partial_and_merge_match_oracle(gu, B, H, Sq, Skv, D, cuts, masked):
     _assert_close(gu.to_f64(merged), OA.attention(qf, kf, vf, mask), "merged")
 
 
-def test_chunked_kv_arrival_full_size_sampled(gu):
-    """Image CP4 share with the gathered K/V arriving in four chunks of one rank's rows."""
+def test_chunked_kv_arrival_full_size_whole(gu):
+    """Image CP4 share with the gathered K/V arriving in four chunks of one rank's rows:
+    every element of the merged output against the oracle."""
     import context_attention_diffusion_amd as cp
+    from oracle_ref import workload_attention
     wl = workloads.WORKLOADS["image_cp4"]
     q, k, v = workloads.global_qkv(wl)
     q = np.ascontiguousarray(q[:, :wl.attn_rows])
@@ -433,10 +413,7 @@ def test_chunked_kv_arrival_full_size_sampled(gu):
     torch.cuda.synchronize()
     got, whole = gu.to_f64(merged), gu.to_f64(dense)
     assert np.abs(got - whole).max() <= 2e-2
-    rng = np.random.default_rng(wl.seed + 11)
-    rows = [(0, int(rng.integers(wl.attn_rows)), int(rng.integers(wl.H))) for _ in range(32)]
-    ref = OA.attention_rows(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), rows)
-    _assert_close(np.stack([got[b, i, h] for b, i, h in rows]), ref, "chunked image_cp4 sampled")
+    _assert_close(got, workload_attention("image_cp4", 0, wl.attn_rows, wl.attn_heads), "chunked image_cp4 whole")
 
 
 # ------------------------------------------------- joint text/image key segments
@@ -479,7 +456,7 @@ def test_joint_segments_match_oracle(gu, B, H, Sq, S_img, T, D, front, im_on, jm
 def test_joint_cfg_workload_segments(gu):
     """The joint CFG workload as two segments (4096 image keys, 512 text keys with the
     per-batch text padding mask): rear layout equals the concatenated masked call bit
-    for bit (same tiles), front layout within the tolerance, sampled rows vs oracle."""
+    for bit (same tiles); the front layout, every element, against the oracle."""
     import context_attention_diffusion_amd as cp
     wl = workloads.WORKLOADS["joint_cfg_cp4"]
     q, k, v = workloads.global_qkv(wl)
@@ -500,11 +477,10 @@ def test_joint_cfg_workload_segments(gu):
     torch.cuda.synchronize()
     assert torch.equal(rear, dense), "rear joint layout differs from the concatenated call"
     assert np.abs(gu.to_f64(front) - gu.to_f64(dense)).max() <= 2e-2
-    rng = np.random.default_rng(wl.seed + 21)
-    rows = [(int(rng.integers(wl.B)), int(rng.integers(wl.attn_rows)), int(rng.integers(wl.H))) for _ in range(32)]
-    ref = OA.attention_rows(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), rows, mask)
-    g = gu.to_f64(front)
-    _assert_close(np.stack([g[b, i, h] for b, i, h in rows]), ref, "joint front sampled")
+    from oracle_ref import workload_attention
+    # the front layout attends the same valid keys in another order: same oracle result
+    _assert_close(gu.to_f64(front), workload_attention(wl.name, 0, wl.attn_rows, wl.attn_heads),
+                  "joint front whole output")
 
 
 @pytest.mark.parametrize("B,H,Sq,Skv,D,cuts,masked", [

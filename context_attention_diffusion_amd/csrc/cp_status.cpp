@@ -14,7 +14,7 @@ extern "C" const char* cp_status_string(int status) {
     case CP_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
     case CP_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case CP_ERR_SCALE: return "softmax scale must be finite and > 0";
-    case CP_ERR_UNSUPPORTED: return "unsupported request (causal attention, unknown phase, or too many ranks)";
+    case CP_ERR_UNSUPPORTED: return "unsupported request (unknown phase or layout flag, or too many ranks)";
     case CP_ERR_HIP: return "HIP runtime error while enqueueing the kernel";
     case CP_ERR_WORKSPACE: return "attention workspace too small (see cp_attn_workspace_bytes)";
     default: return "unknown status code";

@@ -11,6 +11,7 @@ from .ops import (  # noqa: F401
     clear_staging,
     cp_attn_joint,
     cp_attn_localq_globalkv,
+    cp_attn_localq_globalkv_noalloc,
     cp_attn_merge,
     cp_attn_partial,
     cp_attn_partial_accum,
@@ -31,5 +32,5 @@ from .ops import (  # noqa: F401
 __all__ = [
     "CpError", "load", "staging_buffer", "clear_staging",
     "cp_pack_qkv_dst_major", "cp_pack_qkv_dst_major_padded", "cp_output_merge_cropped", "cp_sim_exchange", "cp_unpack_head_sharded",
-    "cp_attn_localq_globalkv", "cp_attn_joint", "cp_attn_partial", "cp_attn_partial_accum", "cp_attn_merge", "cp_attn_recv_to_send", "cp_attn_recv_to_send_2d", "cp_attn_varlen", "cp_varlen_remap_cu_seqlens_q", "cp_attn_workspace_bytes", "cp_output_reverse",
+    "cp_attn_localq_globalkv", "cp_attn_localq_globalkv_noalloc", "cp_attn_joint", "cp_attn_partial", "cp_attn_partial_accum", "cp_attn_merge", "cp_attn_recv_to_send", "cp_attn_recv_to_send_2d", "cp_attn_varlen", "cp_varlen_remap_cu_seqlens_q", "cp_attn_workspace_bytes", "cp_output_reverse",
 ]

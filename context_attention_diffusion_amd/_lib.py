@@ -32,6 +32,8 @@ SIGNATURES = {
                                                   _i64, ctypes.c_float, _vp,
                                                   ctypes.c_size_t, _vp]),
     "cp_attn_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64]),
+    "cp_attn_localq_globalkv_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                                       _i64, ctypes.c_float, _vp]),
     "cp_pack_qkv_dst_major_padded": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                                     _i64, ctypes.c_int, _vp]),
     "cp_output_merge_cropped": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -67,10 +69,11 @@ CP_ERR_SCALE = 8
 CP_ERR_UNSUPPORTED = 9
 CP_ERR_HIP = 10
 CP_ERR_WORKSPACE = 11
+CP_ERR_SCRATCH = 12
 
 CP_DTYPE_BF16 = 0
 CP_DTYPE_FP16 = 1
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 _lib = None
 

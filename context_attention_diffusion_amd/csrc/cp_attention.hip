@@ -64,10 +64,19 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
 #include "cp_common.hpp"
+
+// Scratch memory of cp_attn_localq_globalkv_noalloc, for callers that cannot
+// allocate: the split-KV partial states (one 128 x (D + 2) fp32 slot per part,
+// at most one part per compute unit), sized for D = 128 on up to 256 compute
+// units.  Every device the library runs on holds its own copy until the process
+// ends.  Host code never uses this name as an address: it asks each device for
+// the array's address once (scratch_on_device below).
+static __device__ __align__(256) unsigned char scratch[CP_ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace cpattn {
 namespace {
@@ -1244,10 +1253,29 @@ int attn_check(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D, float s
   return CP_OK;
 }
 
-// Local-Q / global-KV attention on dense [B][S][H][D] operands.
+// Device address of the scratch array on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_on_device(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CP_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return CP_ERR_HIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return CP_OK;
+}
+
+// Local-Q / global-KV attention on dense [B][S][H][D] operands.  static_scratch:
+// the split-KV partial states go to the library's scratch array (ws unused).
 int attn_run(const void* q, const void* k, const void* v, const uint8_t* key_mask, void* o, int64_t B,
              int64_t Sq, int64_t Skv, int64_t H, int64_t D, float scale, void* ws, size_t ws_bytes,
-             cp_stream_t stream) {
+             cp_stream_t stream, bool static_scratch = false) {
   if (!q || !k || !v || !o) return CP_ERR_NULL;
   if (const int st = attn_check(B, Sq, Skv, H, D, scale)) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return CP_ERR_ALIGNMENT;
@@ -1266,9 +1294,15 @@ int attn_run(const void* q, const void* k, const void* v, const uint8_t* key_mas
   const size_t qb = size_t(qe) * 2, kb = size_t(ke) * 2;
   if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb)) return CP_ERR_ALIAS;
   if (key_mask && overlaps(o, qb, key_mask, size_t(B * Skv))) return CP_ERR_ALIAS;
-  return attn_launch(static_cast<const __bf16*>(q), plain_view(Sq, H, D), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), plain_view(Skv, H, D), key_mask, static_cast<__bf16*>(o),
-                     plain_view(Sq, H, D), B, Sq, Skv, H, D, scale, ws, ws_bytes, qb, kb, qb, stream);
+  if (static_scratch) {
+    if (const int st = scratch_on_device(&ws)) return st;
+    ws_bytes = CP_ATTN_NOALLOC_SCRATCH_BYTES;
+  }
+  const int st = attn_launch(static_cast<const __bf16*>(q), plain_view(Sq, H, D), static_cast<const __bf16*>(k),
+                             static_cast<const __bf16*>(v), plain_view(Skv, H, D), key_mask,
+                             static_cast<__bf16*>(o), plain_view(Sq, H, D), B, Sq, Skv, H, D, scale, ws, ws_bytes,
+                             qb, kb, qb, stream);
+  return static_scratch && st == CP_ERR_WORKSPACE ? CP_ERR_SCRATCH : st;
 }
 
 }  // namespace
@@ -1285,6 +1319,13 @@ extern "C" int cp_attn_localq_globalkv_ws(const void* q, const void* k, const vo
                                           int64_t Skv, int64_t H, int64_t D, float scale,
                                           void* workspace, size_t workspace_bytes, cp_stream_t stream) {
   return attn_run(q, k, v, key_mask, o, B, Sq, Skv, H, D, scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" int cp_attn_localq_globalkv_noalloc(const void* q, const void* k, const void* v,
+                                               const uint8_t* key_mask, void* o, int64_t B, int64_t Sq,
+                                               int64_t Skv, int64_t H, int64_t D, float scale,
+                                               cp_stream_t stream) {
+  return attn_run(q, k, v, key_mask, o, B, Sq, Skv, H, D, scale, nullptr, 0, stream, true);
 }
 
 extern "C" int cp_varlen_remap_cu_seqlens_q(const int32_t* cu_q_global, int32_t* cu_q_local, int64_t n_docs,

@@ -17,6 +17,7 @@ extern "C" const char* cp_status_string(int status) {
     case CP_ERR_UNSUPPORTED: return "unsupported request (unknown phase or layout flag, or too many ranks)";
     case CP_ERR_HIP: return "HIP runtime error while enqueueing the kernel";
     case CP_ERR_WORKSPACE: return "attention workspace too small (see cp_attn_workspace_bytes)";
+    case CP_ERR_SCRATCH: return "problem needs more than the library's static scratch array (CP_ATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status code";
   }
 }

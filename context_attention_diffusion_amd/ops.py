@@ -210,6 +210,34 @@ def cp_attn_localq_globalkv(q, k, v, key_mask=None, scale=None, out=None,
     return out
 
 
+def cp_attn_localq_globalkv_noalloc(q, k, v, key_mask=None, scale=None, out=None, stream=None) -> torch.Tensor:
+    """The split-KV attention with its partial states in the library's static scratch
+    array (no workspace, no allocation inside the call; out must be given by callers
+    that cannot allocate).  Same arguments and result as cp_attn_localq_globalkv."""
+    lib = _lib.load()
+    B, Sq, H, D = q.shape
+    Skv = k.shape[1]
+    if k.shape != (B, Skv, H, D) or v.shape != k.shape:
+        raise ValueError("k, v must be [B, Skv, H, D] matching q")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("attention takes bfloat16 q, k, v")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    mask_ptr = None
+    if key_mask is not None:
+        if key_mask.dtype not in (torch.uint8, torch.bool) or tuple(key_mask.shape) != (B, Skv):
+            raise ValueError("key_mask must be uint8/bool [B, Skv]")
+        mask_ptr = _dev(key_mask, "key_mask")
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    _lib.check("cp_attn_localq_globalkv_noalloc", lib.cp_attn_localq_globalkv_noalloc(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), mask_ptr, _dev(out, "o"),
+        B, Sq, Skv, H, D, float(scale), _stream(stream)))
+    return out
+
+
 def cp_attn_joint(q, k_img, v_img, k_joint=None, v_joint=None, img_mask=None, joint_mask=None,
                   joint_front=False, scale=None, out=None, stream=None, split=True,
                   workspace=None) -> torch.Tensor:

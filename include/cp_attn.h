@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CP_ABI_VERSION 10
+#define CP_ABI_VERSION 11
 
 typedef struct ihipStream_t* cp_stream_t; /* == hipStream_t */
 
@@ -70,7 +70,8 @@ enum cp_status {
   CP_ERR_SCALE = 8,        /* softmax scale is not finite or not > 0 */
   CP_ERR_UNSUPPORTED = 9,  /* a valid but unsupported request (bad phase or layout flag, W too large) */
   CP_ERR_HIP = 10,         /* the HIP runtime rejected the launch */
-  CP_ERR_WORKSPACE = 11    /* the workspace is too small (see cp_attn_workspace_bytes) */
+  CP_ERR_WORKSPACE = 11,   /* the workspace is too small (see cp_attn_workspace_bytes) */
+  CP_ERR_SCRATCH = 12      /* the problem needs more than the library's static scratch array */
 };
 
 enum cp_dtype { CP_DTYPE_BF16 = 0, CP_DTYPE_FP16 = 1 };
@@ -216,6 +217,30 @@ int cp_attn_localq_globalkv_ws(const void* q, const void* k, const void* v,
                                int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D,
                                float scale, void* workspace, size_t workspace_bytes,
                                cp_stream_t stream);
+
+/*
+ * The same attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * split-KV partial states live in a static device array of
+ * CP_ATTN_NOALLOC_SCRATCH_BYTES bytes inside the library (one 128 x 130 fp32
+ * slot per compute unit for up to 256 compute units), of which each device holds
+ * its own copy from the first call on it until the process ends.  Arguments,
+ * results and conditions are those of cp_attn_localq_globalkv_ws, and the
+ * results are bit-identical to it.  The call allocates and frees nothing.
+ *
+ * A problem whose split would need more scratch than the array holds (only on a
+ * device with more than 256 compute units) is rejected with CP_ERR_SCRATCH
+ * before anything is enqueued.  All calls on one device share that device's
+ * array and leave their partial states in it (nothing in it needs to start
+ * cleared: every slot a call reads it has written first), so two calls that
+ * can overlap on one device -- on two streams without ordering, or from two
+ * host threads -- race.  Calls on one stream are safe.
+ */
+#define CP_ATTN_NOALLOC_SCRATCH_BYTES (256u * 128u * 130u * 4u)
+int cp_attn_localq_globalkv_noalloc(const void* q, const void* k, const void* v,
+                                    const uint8_t* key_mask, void* o,
+                                    int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D,
+                                    float scale, cp_stream_t stream);
 
 /*
  * Bytes of workspace cp_attn_localq_globalkv_ws may use for this problem on

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings():
     lib = _lib.load()
     seen = set()
-    for code in range(0, 12):
+    for code in range(0, 13):
         s = lib.cp_status_string(code).decode()
         assert s and s not in seen
         seen.add(s)
@@ -109,6 +109,14 @@ def _attn_ws(**kw):
     return _lib.load().cp_attn_localq_globalkv_ws(a["q"], a["k"], a["v"], a["m"], a["o"], a["B"],
                                                   a["Sq"], a["Skv"], a["H"], a["D"], a["scale"],
                                                   a["ws"], a["nbytes"], None)
+
+
+def _attn_noalloc(**kw):
+    a = dict(q=A, k=A + BIG, v=A + 2 * BIG, m=None, o=A + 3 * BIG, B=1, Sq=8, Skv=16, H=2,
+             D=128, scale=0.125)
+    a.update(kw)
+    return _lib.load().cp_attn_localq_globalkv_noalloc(a["q"], a["k"], a["v"], a["m"], a["o"], a["B"],
+                                                       a["Sq"], a["Skv"], a["H"], a["D"], a["scale"], None)
 
 
 def _fused(**kw):
@@ -254,6 +262,31 @@ def test_attention_rejects(kw, code):
 ])
 def test_attention_ws_rejects(kw, code):
     assert _attn_ws(**kw) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.CP_ERR_NULL),
+    (dict(Sq=0), _lib.CP_ERR_SHAPE),
+    (dict(D=96), _lib.CP_ERR_HEAD_DIM),
+    (dict(scale=-1.0), _lib.CP_ERR_SCALE),
+    (dict(k=A + BIG + 8), _lib.CP_ERR_ALIGNMENT),
+    (dict(o=A + 2 * BIG + 16), _lib.CP_ERR_ALIAS),   # o overlaps v
+    (dict(B=1 << 31), _lib.CP_ERR_SHAPE),
+])
+def test_attention_noalloc_rejects(kw, code):
+    """Host validation runs before the library looks up its scratch array."""
+    assert _attn_noalloc(**kw) == code
+
+
+def test_noalloc_scratch_limit_matches_the_workspace_bound():
+    """The static scratch holds the largest split any 256-CU device plans for D = 128:
+    one 128 x (D + 2) fp32 slot per compute unit."""
+    text = open(HEADER).read()
+    m = re.search(r"#define CP_ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u \* (\d+)u \* (\d+)u \* (\d+)u\)", text)
+    assert m
+    cus, rows, cols, word = (int(x) for x in m.groups())
+    assert (cus, rows, cols, word) == (256, 128, 128 + 2, 4)
 
 
 @cpu_only

@@ -326,6 +326,61 @@ def oracle_attention(wl, full, mask):
     return ref, time.perf_counter() - t
 
 
+def layout_ramp(dev, seqs=(256, 1088, 4352, 17408, 69632), H=24, D=128, W=4):
+    """Pack kernel and a plain device copy of the same bytes, cold, over a range of
+    sizes (one rank of an H=24, D=128, W=4 layout with S_local rows): the time of one
+    launch against its algorithmic bytes, and the least-squares fit
+    t = t0 + bytes / bw_sustained over the sizes, i.e. the fixed per-launch cost and
+    the streaming bandwidth.  Read sets smaller than 600 MB rotate over enough buffer
+    sets to miss the 256 MB Infinity Cache."""
+    import torch
+
+    import context_attention_diffusion_amd as cp
+
+    rows = []
+    for Sl in seqs:
+        nbytes = 2 * 3 * Sl * H * D * 2
+        read = nbytes // 2
+        nsets = max(1, int(math.ceil(600e6 / read))) if read < 600e6 else 1
+        nsets = max(nsets, 2)
+        sets = []
+        for _ in range(nsets):
+            x = [torch.empty((1, Sl, H, D), dtype=torch.bfloat16, device=dev).normal_() for _ in range(3)]
+            st = torch.empty((W, Sl, H // W, 3 * D), dtype=torch.bfloat16, device=dev)
+            sets.append((x, st, torch.empty_like(st)))
+        rec = {"S_local": Sl, "bytes": nbytes}
+        for which in ("pack", "copy"):
+            def launch(sset):
+                x, st, cpy = sset
+                if which == "pack":
+                    cp.cp_pack_qkv_dst_major(*x, W, staging=st)
+                else:
+                    cpy.copy_(st)
+            for sset in sets:
+                launch(sset)
+            torch.cuda.synchronize()
+            rounds = max(1, int(40 // nsets))
+            order = [sets[i % nsets] for i in range(rounds * nsets)]
+            it = iter(order * 2)
+            ms = time_burst(lambda: launch(next(it)), len(order))
+            rec[f"{which}_us"] = ms * 1e3
+            rec[f"{which}_GBps"] = nbytes / (ms * 1e-3) / 1e9
+        rows.append(rec)
+        del sets
+        torch.cuda.empty_cache()
+    res = {"H": H, "D": D, "W": W, "sizes": rows}
+    for which in ("pack", "copy"):
+        x = np.array([r["bytes"] for r in rows], dtype=np.float64)
+        y = np.array([r[f"{which}_us"] for r in rows], dtype=np.float64) * 1e-6
+        A = np.stack([np.ones_like(x), x], axis=1)
+        (t0, inv_bw), *_ = np.linalg.lstsq(A, y, rcond=None)
+        res[f"{which}_fixed_us"] = float(t0 * 1e6)
+        res[f"{which}_sustained_GBps"] = float(1.0 / inv_bw / 1e9)
+    res["note"] = ("t = fixed + bytes / sustained fitted over the sizes; at a workload's pack bytes the "
+                   "attainable GB/s of a single launch is bytes / (fixed + bytes / sustained)")
+    return res
+
+
 def cpu_baseline(wl, flops, seconds):
     return {
         "value": flops / seconds / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
@@ -993,6 +1048,8 @@ def main():
         del ref
     del graph, path
     torch.cuda.empty_cache()
+    if args.only is None and not args.no_cold and not args.no_per_config:
+        out["layout_ramp"] = layout_ramp(dev)
     if args.only is None and not args.no_per_config:
         per = {}
         for name in PER_CONFIG:

@@ -57,8 +57,9 @@
 // segments with masks of their own (joint text/image keys, or the other
 // AllGather rank's K/V); 8 = a second segment with a row stride of its own;
 // 16 = packed documents (varlen: query document i against key document i, the
-// boundaries read from device memory).  Split-KV and the partial / accumulating
-// outputs are run-time paths of the same kernel, with a separate merge kernel.
+// boundaries read from device memory); 32 = split-KV (the key range of each
+// query block cut over nsplit workgroups, whose partial states a separate
+// kernel merges).  The partial / accumulating outputs are run-time paths.
 
 #include <hip/hip_runtime.h>
 
@@ -197,6 +198,7 @@ constexpr int kModeTwoSeg = 2;
 constexpr int kModeCross = 4;
 constexpr int kModeSeg1Rows = 8;  // segment 1 has a view (row stride) of its own
 constexpr int kModeVarlen = 16;   // packed documents: batch index b is document b
+constexpr int kModeSplit = 32;    // the key range of each query block split over nsplit workgroups
 
 // CHUNKED = false: every view of the kernel is plain.  CHUNKED = true: a view may
 // be chunked (each view says whether it is).
@@ -268,6 +270,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   static_assert(!kSeg1Rows || kTwoSeg, "a view of its own for segment 1 needs two segments");
   constexpr bool kVarlen = (MODE & kModeVarlen) != 0;
   static_assert(!kVarlen || MODE == kModeVarlen, "packed documents use plain views and one key segment");
+  constexpr bool kSplit = (MODE & kModeSplit) != 0;
   using C = Cfg<D>;
   // K and V tiles: one array per (operand, key group, buffer).  Separate objects
   // let the compiler see that a fill of one buffer does not alias the reads of
@@ -820,7 +823,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
     const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
     const float l_tot = pair_sum(a0 * l_run + a1 * l1);
-    if (slot_idx >= 0) {
+    if (kSplit && slot_idx >= 0) {
       // partial state of this segment: unnormalized O (relative to mm), mm, l
       const size_t prow = size_t(slot_idx) * C::BM + gw * 32 + l32;
       float* wp = a.ws + prow * D;
@@ -949,7 +952,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // has rows there too, so that two documents sharing a tile run side by side.
   const bool vslot1 = kVarlen && int(blockIdx.x) >= a.n_work;
   const int pid = vslot1 ? int(blockIdx.x) - a.n_work : int(blockIdx.x);
-  const int n = kVarlen ? a.n_work : a.n_work * a.nsplit;
+  const int n = kSplit ? a.n_work * a.nsplit : a.n_work;
   const int per = n / kNumXcd, rem = n % kNumXcd;
   const int xcd = pid % kNumXcd, local = pid / kNumXcd;
   const int logical =
@@ -979,7 +982,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       while (lo < a.B && end_of(lo) <= start_of(lo) && start_of(lo) < r0 + C::BM) ++lo;
       if (lo < a.B && start_of(lo) < r0 + C::BM && end_of(lo) > start_of(lo)) process(logical, 0, 0, -1, lo);
     }
-  } else if (a.nsplit == 1) {
+  } else if constexpr (!kSplit) {
     process(logical, 0, n_iter_blk, -1, 0);
   } else {
     const int j = logical % a.nsplit;
@@ -1213,10 +1216,19 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
   const int mode = (chunked ? kModeChunked : 0) | (seg1 ? kModeTwoSeg : 0) |
                    ((kv.chunked && kv.L.d % 64 != 0) || (seg1 && args.kv1.chunked && args.kv1.L.d % 64 != 0)
                         ? kModeCross : 0) |
-                   (seg1_rows ? kModeSeg1Rows : 0) | (cu_q ? kModeVarlen : 0);
+                   (seg1_rows ? kModeSeg1Rows : 0) | (cu_q ? kModeVarlen : 0) | (args.nsplit > 1 ? kModeSplit : 0);
   auto launch_fwd = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, args); };
   if (D == 128) {
     if (mode == 0) launch_fwd(attn_fwd_kernel<128, 0>);
+    else if (mode == kModeSplit) launch_fwd(attn_fwd_kernel<128, kModeSplit>);
+    else if (mode == kModeChunked + kModeSplit) launch_fwd(attn_fwd_kernel<128, kModeChunked + kModeSplit>);
+    else if (mode == kModeChunked + kModeCross + kModeSplit) launch_fwd(attn_fwd_kernel<128, kModeChunked + kModeCross + kModeSplit>);
+    else if (mode == kModeTwoSeg + kModeSplit) launch_fwd(attn_fwd_kernel<128, kModeTwoSeg + kModeSplit>);
+    else if (mode == kModeTwoSeg + kModeSeg1Rows + kModeSplit) launch_fwd(attn_fwd_kernel<128, kModeTwoSeg + kModeSeg1Rows + kModeSplit>);
+    else if (mode == kModeChunked + kModeTwoSeg + kModeSeg1Rows + kModeSplit)
+      launch_fwd(attn_fwd_kernel<128, kModeChunked + kModeTwoSeg + kModeSeg1Rows + kModeSplit>);
+    else if (mode == kModeChunked + kModeTwoSeg + kModeCross + kModeSeg1Rows + kModeSplit)
+      launch_fwd(attn_fwd_kernel<128, kModeChunked + kModeTwoSeg + kModeCross + kModeSeg1Rows + kModeSplit>);
     else if (mode == kModeVarlen) launch_fwd(attn_fwd_kernel<128, kModeVarlen>);
     else if (mode == kModeChunked) launch_fwd(attn_fwd_kernel<128, kModeChunked>);
     else if (mode == kModeChunked + kModeCross) launch_fwd(attn_fwd_kernel<128, kModeChunked + kModeCross>);
@@ -1230,6 +1242,15 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
     if (args.nsplit > 1) hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, cblock, 0, s, args);
   } else {
     if (mode == 0) launch_fwd(attn_fwd_kernel<64, 0>);
+    else if (mode == kModeSplit) launch_fwd(attn_fwd_kernel<64, kModeSplit>);
+    else if (mode == kModeChunked + kModeSplit) launch_fwd(attn_fwd_kernel<64, kModeChunked + kModeSplit>);
+    else if (mode == kModeChunked + kModeCross + kModeSplit) launch_fwd(attn_fwd_kernel<64, kModeChunked + kModeCross + kModeSplit>);
+    else if (mode == kModeTwoSeg + kModeSplit) launch_fwd(attn_fwd_kernel<64, kModeTwoSeg + kModeSplit>);
+    else if (mode == kModeTwoSeg + kModeSeg1Rows + kModeSplit) launch_fwd(attn_fwd_kernel<64, kModeTwoSeg + kModeSeg1Rows + kModeSplit>);
+    else if (mode == kModeChunked + kModeTwoSeg + kModeSeg1Rows + kModeSplit)
+      launch_fwd(attn_fwd_kernel<64, kModeChunked + kModeTwoSeg + kModeSeg1Rows + kModeSplit>);
+    else if (mode == kModeChunked + kModeTwoSeg + kModeCross + kModeSeg1Rows + kModeSplit)
+      launch_fwd(attn_fwd_kernel<64, kModeChunked + kModeTwoSeg + kModeCross + kModeSeg1Rows + kModeSplit>);
     else if (mode == kModeVarlen) launch_fwd(attn_fwd_kernel<64, kModeVarlen>);
     else if (mode == kModeChunked) launch_fwd(attn_fwd_kernel<64, kModeChunked>);
     else if (mode == kModeChunked + kModeCross) launch_fwd(attn_fwd_kernel<64, kModeChunked + kModeCross>);

@@ -803,6 +803,8 @@ def uaa_compare(seqs, heads=14, D=128, seed=1240):
 
 
 ATTN_SRC = os.path.join(ROOT, "context_attention_diffusion_amd", "csrc", "cp_attention.hip")
+# flags of the counter runs: only the attention kernel's launches, no extra sections
+PROFILE_ATTN_FLAGS = "--only attn --steps 5 --warmup 1 --eager --no-cold --no-cpu-baseline --no-per-config"
 CALIB_BYTES = 256 << 20
 
 
@@ -843,9 +845,9 @@ def summarize_traffic(fetch_dir, write_dir, out_json, workload):
            "traffic_bytes": (f_attn * sf + w_attn * sw) * 1024.0,
            "commands": [
                f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir}/attn -o p --output-format csv -- python3 bench.py "
-               f"--workload {workload} --only attn --steps 5 --warmup 1 --eager",
+               f"--workload {workload} {PROFILE_ATTN_FLAGS}",
                f"rocprofv3 --pmc WRITE_SIZE -d {write_dir}/attn -o p --output-format csv -- python3 bench.py "
-               f"--workload {workload} --only attn --steps 5 --warmup 1 --eager",
+               f"--workload {workload} {PROFILE_ATTN_FLAGS}",
                f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir}/copy -o p --output-format csv -- python3 bench.py "
                "--calib-copy",
                f"rocprofv3 --pmc WRITE_SIZE -d {write_dir}/copy -o p --output-format csv -- python3 bench.py "
@@ -886,8 +888,7 @@ def summarize_mfma(pmc_dir, out_md, workload):
         "",
         "```",
         f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE "
-        f"-d {pmc_dir} -o p --output-format csv -- python3 bench.py --workload {workload} --only attn --steps 5 "
-        f"--warmup 1 --eager --no-cold --no-cpu-baseline",
+        f"-d {pmc_dir} -o p --output-format csv -- python3 bench.py --workload {workload} {PROFILE_ATTN_FLAGS}",
         f"python3 bench.py --workload {workload} --summarize-mfma {pmc_dir} {out_md}",
         "```",
         "",

@@ -90,6 +90,36 @@ def test_scale_and_large_logits(gu):
         _assert_close(got, ref, f"scale {scale}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("big_half", [0, 1])
+@pytest.mark.parametrize("mask_first", [False, True])
+def test_scores_rising_past_the_running_max(gu, D, big_half, mask_first):
+    """Keys whose scores jump well past every earlier key's in the middle of the
+    sequence (softmax taken against an older running max until the probabilities
+    grow too large): tiles 0-1 at 0, tiles 2-3 with one 32-key half at +30 and
+    the other at +27, later tiles at +29, in log2 units of the softmax.  Both
+    halves of tiles 2-3 and the later tiles carry weight in the result."""
+    B, Sq, Skv, H = 1, 130, 613, 2
+    rng = np.random.default_rng(90 + D + 2 * big_half + 4 * int(mask_first))
+    j = np.arange(Skv)
+    tile, half = j // 64, (j % 64) // 32
+    level = np.where(tile < 2, 0.0, np.where(tile < 4, np.where(half == big_half, 30.0, 27.0), 29.0))
+    q = rng.standard_normal((B, Sq, H, D)) * 0.1
+    q[..., 0] = (1.0 + 0.1 * np.arange(Sq) / Sq)[None, :, None]
+    k = rng.standard_normal((B, Skv, H, D)) * 0.1
+    k[..., 0] = (level / math.log2(math.e))[None, :, None]
+    v = rng.standard_normal((B, Skv, H, D))
+    qb, kb, vb = bf16.f64_to_bits_rne(q), bf16.f64_to_bits_rne(k), bf16.f64_to_bits_rne(v)
+    mask = None
+    if mask_first:
+        mask = np.ones((B, Skv), np.uint8)
+        mask[:, :128] = 0
+    print(f"[attn] rising scores D={D} big_half={big_half} mask_first={mask_first}", flush=True)
+    got = _run(gu, qb, kb, vb, mask, scale=1.0)
+    ref = OA.attention(bf16.bits_to_f64(qb), bf16.bits_to_f64(kb), bf16.bits_to_f64(vb), mask, 1.0)
+    _assert_close(got, ref, f"rising D{D} h{big_half} m{int(mask_first)}")
+
+
 def test_mask_closed_forms(gu):
     B, Sq, Skv, H, D = 3, 70, 150, 2, 128
     q = _rand_bits((B, Sq, H, D), 51)

@@ -106,6 +106,10 @@ def test_graph_replay_fused_split_and_packed_paths():
     o = torch.empty_like(q)
     ws = torch.zeros(cp.cp_attn_workspace_bytes(1, 130, 4096, 2, 128), dtype=torch.uint8, device="cuda:0")
     _replays_match(lambda: cp.cp_attn_localq_globalkv(q, k, v, None, out=o, workspace=ws), [o], "split-KV")
+    # the same split through the library's own scratch array (nothing allocated per call)
+    o2 = torch.empty_like(q)
+    _replays_match(lambda: cp.cp_attn_localq_globalkv_noalloc(q, k, v, out=o2), [o2], "split-KV, no allocation")
+    assert torch.equal(o2, o)
     # fused receive -> send, Ulysses W = 2, B = 2 (chunked rows)
     W, B, Sl, Hl, D = 2, 2, 70, 3, 128
     recv = _randn((W, B * Sl, Hl, 3 * D), 4)

@@ -827,16 +827,24 @@ def traffic_file(workload):
     return os.path.join(ROOT, "profiles", f"traffic_attn_fwd_{workload}.json")
 
 
-def read_counter_csv(d, counter, kernel_substr):
-    """Mean per-dispatch value of `counter` for kernels whose name contains kernel_substr."""
+def read_counter_by_kernel(d, counter, kernel_substr):
+    """Mean per-dispatch value of `counter` for each kernel whose name contains kernel_substr."""
     import csv
     import glob
-    vals = []
+    vals = {}
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
-                vals.append(float(r["Counter_Value"]))
-    return float(np.mean(vals)) if vals else None
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: float(np.mean(v)) for k, v in vals.items()}
+
+
+def read_counter_csv(d, counter, kernel_substr):
+    """Per-call value of `counter` over the kernels whose name contains kernel_substr:
+    the sum of each kernel's mean per dispatch (an attention call launches each of its
+    kernels once, e.g. a 256-row and a 128-row launch over different heads)."""
+    per = read_counter_by_kernel(d, counter, kernel_substr)
+    return float(sum(per.values())) if per else None
 
 
 def summarize_traffic(fetch_dir, write_dir, out_json, workload):
@@ -902,8 +910,9 @@ def summarize_mfma(pmc_dir, out_md, workload):
         f"python3 bench.py --workload {workload} --summarize-mfma {pmc_dir} {out_md}",
         "```",
         "",
-        f"Per attn_fwd_kernel dispatch (mean over the dispatches of the run; {n_xcd} XCDs, {n_cu} CUs, "
-        f"{simds} SIMDs; the profiler serialises dispatches):",
+        f"Per attention call: each attn_fwd_kernel launch's mean per dispatch over the run, summed over the "
+        f"launches of one call ({', '.join(sorted(short_kernel(k) for k in read_counter_by_kernel(pmc_dir, 'GRBM_GUI_ACTIVE', 'attn_fwd')))}; "
+        f"{n_xcd} XCDs, {n_cu} CUs, {simds} SIMDs; the profiler serialises dispatches):",
         "",
         "| quantity | value |",
         "|---|---|",
@@ -925,10 +934,16 @@ def summarize_mfma(pmc_dir, out_md, workload):
     print("\n".join(lines))
 
 
+def short_kernel(name):
+    return name.replace("void ", "").replace("cpattn::(anonymous namespace)::", "").split("(")[0]
+
+
 def summarize_trace(db_path, out_md, command, workload):
     """Per-kernel launch counts and durations from a rocprofv3 kernel-trace database
-    (its top_kernels view: durations in microseconds), with the attention kernel's
-    algorithmic TFLOP/s and fraction of the dense bf16 peak at that average."""
+    (its top_kernels view: durations in microseconds), with the attention call's
+    algorithmic TFLOP/s and fraction of the dense bf16 peak: the call's time is the sum
+    of the averages of its attn_fwd_kernel launches when they run equally often (one
+    call launches each once), else the average of the busiest one."""
     import sqlite3
     import workloads
     wl = workloads.WORKLOADS[workload]
@@ -939,17 +954,19 @@ def summarize_trace(db_path, out_md, command, workload):
     lines = [f"# Kernel trace: workload {workload}", "", "Command (repository root, one MI355X):", "", "```",
              command, f"python3 bench.py --workload {workload} --summarize-trace <trace db> <this file> '<command>'",
              "```", "", "| kernel | launches | total us | average us | share of GPU time |", "|---|---|---|---|---|"]
-    def short(name):
-        return name.replace("void ", "").replace("cpattn::(anonymous namespace)::", "").split("(")[0]
-
     for name, n, tot, avg, pct in rows:
-        lines.append(f"| `{short(name)}` | {n} | {tot:.1f} | {avg:.3f} | {pct:.2f}% |")
+        lines.append(f"| `{short_kernel(name)}` | {n} | {tot:.1f} | {avg:.3f} | {pct:.2f}% |")
     attn = [r for r in rows if "attn_fwd_kernel" in r[0]]
     if attn:
-        name, n, tot, avg, pct = max(attn, key=lambda r: r[2])
+        if len({r[1] for r in attn}) == 1:
+            used = attn
+        else:
+            used = [max(attn, key=lambda r: r[2])]
+        avg = sum(r[3] for r in used)
+        names = " + ".join(f"`{short_kernel(r[0])}`" for r in used)
         tf = flops / (avg * 1e-6) / 1e12
-        lines += ["", f"Attention (`{short(name)}`): {flops / 1e9:.2f} GFLOP per launch "
-                  f"(4 B H Sq Skv D over valid keys) / {avg:.2f} us average = {tf:.1f} TFLOP/s = "
+        lines += ["", f"Attention call ({names}): {flops / 1e9:.2f} GFLOP "
+                  f"(4 B H Sq Skv D over valid keys) / {avg:.2f} us = {tf:.1f} TFLOP/s = "
                   f"{100.0 * tf / PEAK_BF16_TFLOPS:.1f}% of the 2.5 PFLOP/s dense bf16 peak."]
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -1133,7 +1150,10 @@ def measure_config(path, args, step_fn):
                            "frac": kern["attn"]["TFLOPs"] / PEAK_BF16_TFLOPS, "traffic": traffic,
                            "kernel": "attn_fwd_kernel",
                            "algorithmic_flops_per_launch": flops,
-                           "launches_per_timed_replay": KERNEL_BURST}
+                           "launches_per_timed_replay": KERNEL_BURST,
+                           "note": "per cp_attn_localq_globalkv call: a call whose heads the library splits "
+                                   "between 256-row and 128-row blocks launches attn_fwd_kernel twice, and "
+                                   "achieved is over both"}
     rec["kernels"] = kern
     if args.only is None and not args.no_cold:
         pc, uc, cc = cold_layout_gbps(wl, dev)

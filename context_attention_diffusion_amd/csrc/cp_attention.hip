@@ -48,6 +48,13 @@
 //    applied only to tiles that need it.
 //  * Workgroups are numbered so that all query tiles of one (batch, head) land
 //    on the same XCD, whose L2 then serves that head's K/V to all of them.
+//  * Wide blocks (compile-time bit 64): 256 query rows, the two groups on rows
+//    0-127 and 128-255, both walking every key tile (group 1 still one Q K^T
+//    ahead), so that each tile brought into LDS serves 256 rows: half the L2 ->
+//    LDS traffic per flop, which the chip turns into clock when it runs at its
+//    power limit.  K tiles rotate over four LDS buffers and V tiles over two.  A
+//    call splits its heads between a launch of wide blocks and one of 128-row
+//    blocks so that each launch fills whole rounds of the compute units.
 //
 // Variants (compile-time MODE bits, so that the dense path carries none of the
 // others' scalar state): 1 = operands addressed through strided views whose
@@ -59,7 +66,8 @@
 // 16 = packed documents (varlen: query document i against key document i, the
 // boundaries read from device memory); 32 = split-KV (the key range of each
 // query block cut over nsplit workgroups, whose partial states a separate
-// kernel merges).  The partial / accumulating outputs are run-time paths.
+// kernel merges); 64 = wide blocks (with 0, 1, 5, 2, 10, 11 and 15).  The
+// partial / accumulating outputs are run-time paths.
 
 #include <hip/hip_runtime.h>
 
@@ -199,6 +207,7 @@ constexpr int kModeCross = 4;
 constexpr int kModeSeg1Rows = 8;  // segment 1 has a view (row stride) of its own
 constexpr int kModeVarlen = 16;   // packed documents: batch index b is document b
 constexpr int kModeSplit = 32;    // the key range of each query block split over nsplit workgroups
+constexpr int kModeWide = 64;     // 256-row blocks: the two groups take different rows and share every tile
 
 // CHUNKED = false: every view of the kernel is plain.  CHUNKED = true: a view may
 // be chunked (each view says whether it is).
@@ -271,7 +280,14 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   constexpr bool kVarlen = (MODE & kModeVarlen) != 0;
   static_assert(!kVarlen || MODE == kModeVarlen, "packed documents use plain views and one key segment");
   constexpr bool kSplit = (MODE & kModeSplit) != 0;
+  // Wide block: 256 query rows, group g on rows [128 g, 128 g + 128), both groups on
+  // every key tile (group 1 one Q K^T ahead, as in the 128-row block), so each K/V
+  // tile brought into LDS serves twice the rows.  Not for packed documents or
+  // split-KV parts, and the output is always bf16 O.
+  constexpr bool kWide = (MODE & kModeWide) != 0;
+  static_assert(!kWide || (!kVarlen && !kSplit), "the wide block has no packed-document or split-KV form");
   using C = Cfg<D>;
+  constexpr int BMB = kWide ? 2 * C::BM : C::BM;  // query rows per workgroup
   // K and V tiles: one array per (operand, key group, buffer).  Separate objects
   // let the compiler see that a fill of one buffer does not alias the reads of
   // another, so no wait for the in-flight fills is inserted before those reads.
@@ -286,6 +302,12 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // issued in the same interval, overwrite group 1's K buffer 0 with its third
   // tile; nothing orders those writes after that read.
   __shared__ __attribute__((aligned(1024))) char lds3_k1first[C::TILE];
+  // Wide block: V tile i in buffer i % 2, K tile i in buffer i % 4 (group 0 reads K
+  // tile i and group 1 K tile i + 1 while tile i + 2 is being filled).  The V
+  // buffers again come first, below the K buffers.
+  __shared__ __attribute__((aligned(1024))) char lds0_w_v0[C::TILE], lds0_w_v1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char lds1_w_k0[C::TILE], lds1_w_k1[C::TILE], lds1_w_k2[C::TILE],
+      lds1_w_k3[C::TILE];
 
   const int tid = threadIdx.x;
   // Wave-uniform indices go through readfirstlane so that the compiler keeps
@@ -361,7 +383,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   };
 
   // ---- Q fragment (B operand of S^T = K Q^T): query row q_row, d = ks*16 + 8*hi .. +8
-  const int q_row = mt * C::BM + gw * 32 + l32;
+  const int q_row = mt * BMB + (kWide ? grp * C::BM : 0) + gw * 32 + l32;
   bf16x8 qf[C::KS];
   {
     const bool ok = q_row < Sq && q_row >= q_lo;
@@ -377,10 +399,13 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   const int n_tiles = kTwoSeg ? a.nt0 + (a.Skv1 + C::BN - 1) / C::BN : (Skv + C::BN - 1) / C::BN;
   // iterations of every wave in this segment (a document: all of its key tiles)
   const int n_iter = kVarlen ? (n_tiles + 1) / 2 : i1 - i0;
-  // tiles of key group g in the segment: global tiles 2 (i0 + j) + g < n_tiles
-  auto tiles_of_group = [&](int g) { return min(n_iter, max(0, (n_tiles - g + 1) / 2 - i0)); };
+  // tiles of key group g in the segment: global tiles 2 (i0 + j) + g < n_tiles (wide
+  // block: both groups take every tile, i0 + j < n_tiles)
+  auto tiles_of_group = [&](int g) {
+    return kWide ? min(n_iter, max(0, n_tiles - i0)) : min(n_iter, max(0, (n_tiles - g + 1) / 2 - i0));
+  };
   const int n_g = tiles_of_group(grp);
-  auto tile_of = [&](int i) { return 2 * (i0 + i) + grp; };
+  auto tile_of = [&](int i) { return kWide ? i0 + i : 2 * (i0 + i) + grp; };
 
   // ---- HBM -> LDS fill.  Slot s of a tile (16 bytes) holds chunk
   // (s % CHUNKS) ^ swz(key) of row key = s / CHUNKS; instruction j of wave gw
@@ -497,13 +522,23 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     constexpr int G = decltype(g)::value, B = decltype(bf)::value;
     return G == 0 ? (B == 0 ? lds0_v00 : lds0_v01) : (B == 0 ? lds0_v10 : lds0_v11);
   };
+  // Wide block: K tile buffer B (0..3), V tile buffer B (0..1).
+  auto wktile = [&](auto bf) -> char* {
+    constexpr int B = decltype(bf)::value;
+    return B == 0 ? lds1_w_k0 : B == 1 ? lds1_w_k1 : B == 2 ? lds1_w_k2 : lds1_w_k3;
+  };
+  auto wvtile = [&](auto bf) -> char* {
+    constexpr int B = decltype(bf)::value;
+    return B == 0 ? lds0_w_v0 : lds0_w_v1;
+  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   const int n_g1 = tiles_of_group(1);  // tiles of group 1 (local tile i is global tile 2(i0 + i) + 1)
   // Bias rows: group 0 keeps tile i's row in slot i % 2, group 1 in slot i % 4 (it
   // reads a row one iteration later, at the top of the iteration that uses it, so a
   // row is rewritten only after a barrier has followed its last read).
-  float* bias_row = lds2_bias + grp * 2 * C::BN;
+  // (wide block: one row per tile, slot i % 2, written by group 0 and read by both)
+  float* bias_row = lds2_bias + (kWide ? 0 : grp * 2 * C::BN);
 
   // Key validity of tile t as an additive bias, one key per thread of wave 0.
   // The mask byte is loaded here and only compared when the bias row is
@@ -533,7 +568,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // (the V tiles fill it): the per-step lane addresses are kept kKHigh bytes high,
   // opaque to the optimiser so it cannot fold the constant back, and reads address
   // from tile - kKHigh, so the tile base and the 32-key block fit the offset field.
-  constexpr int kKHigh = 4 * C::TILE >= 65536 ? 65536 : 0;
+  constexpr int kKHigh = kWide ? (6 * C::TILE > 65536 ? 2 * C::TILE : 0) : (4 * C::TILE >= 65536 ? 65536 : 0);
   uint32_t kx[C::KS];
 #pragma unroll
   for (int kk = 0; kk < C::KS; ++kk) {
@@ -649,7 +684,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // kk, fills 3kk .. 3kk+2 of the list (tile f / SPT, instruction f % SPT), so the
   // last ones go out by two thirds of the chain.  Scheduling fences keep the fills
   // in place while MFMAs and LDS reads move freely.
-  auto qk_fills = [&](const char* kt, f32x16* s, const FillSrc* fs, char* const* dst) {
+  auto qk_fills = [&](const char* kt, f32x16* s, const FillSrc* fs, char* const* dst, int n_fill_tiles) {
     f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < C::KS; ++kk) {
@@ -661,7 +696,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 #pragma unroll
       for (int f = 3 * kk; f < 3 * kk + 3 && f < 4 * C::SPT; ++f) {
         const int tile = f / C::SPT, j = f % C::SPT;
-        if (tile < 4) fill_one(fs[tile], j, dst[tile]);
+        if (tile < n_fill_tiles) fill_one(fs[tile], j, dst[tile]);
       }
       __builtin_amdgcn_sched_barrier(0x078F);
     }
@@ -669,6 +704,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     s[1] = acc1;
   };
 
+  if constexpr (!kWide) {
   // ---- prologue.  Group 0 consumes K and V of tile i in iteration i; group 1
   // runs one K tile ahead (its iteration i ends with the scores of tile i+1, whose
   // max it takes at the top of iteration i+1, while group 0 is in its Q K^T).
@@ -728,7 +764,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
                              want[2] ? 2 * (i0 + i + 2) + 1 : tc, want[3] ? 2 * (i0 + i + 1) + 1 : tc};
           const FillSrc fs[4] = {fill_src(1, tl[3]), fill_src(0, tl[0]), fill_src(1, tl[1]), fill_src(0, tl[2])};
           char* const dst[4] = {vtile(I1{}, BQ{}), ktile(I0{}, BQ{}), vtile(I0{}, BQ{}), ktile(I1{}, BP{})};
-          qk_fills(ktile(I0{}, BP{}), sc, fs, dst);
+          qk_fills(ktile(I0{}, BP{}), sc, fs, dst, 4);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (nx) bias_of(tile_of(i + 1));
@@ -790,6 +826,120 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       iter1(I0{}, i);
       if (i + 1 < n_iter) iter1(I1{}, i + 1);
     }
+  }
+  } else {
+  // ---- wide block.  Iteration i: group 0 runs Q K^T of tile i (K buffer i % 4) with
+  // the fills of V tile i + 1 and K tile i + 2 between its steps, then the max,
+  // softmax and P V (V buffer i % 2); group 1 takes the max, softmax and P V of
+  // tile i (scores from the previous iteration), then Q K^T of tile i + 1.  During
+  // iteration i the buffers being filled held V tile i - 1 and K tile i - 2, whose
+  // last reads were in iteration i - 1.  Group 0 issues every fill and writes the
+  // bias rows (tile i in slot i % 2), which both groups read in iteration i.
+  if (grp == 0) {
+    if (n_g > 0) {
+      fill(0, tile_of(0), wktile(I0{}));
+      fill(1, tile_of(0), wvtile(I0{}));
+      bias_of(tile_of(0));
+      store_bias(0);
+    }
+    if (n_g > 1) fill(0, tile_of(1), wktile(I1{}));
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's LDS fills have landed
+  __syncthreads();
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  if (grp == 0) {
+    auto iterw0 = [&](auto par, int i) {
+      constexpr int P = decltype(par)::value;  // i % 4
+      using V0 = std::integral_constant<int, P % 2>;
+      using V1 = std::integral_constant<int, (P + 1) % 2>;
+      using K0 = std::integral_constant<int, P>;
+      using K2 = std::integral_constant<int, (P + 2) % 4>;
+      if (i < n_g) {
+        const bool nx = i + 1 < n_g;
+        {
+          // past the last tile the current one is re-read into a buffer whose
+          // contents nothing uses (group 1's last Q K^T is discarded)
+          const int tc = tile_of(i);
+          const FillSrc fs[2] = {fill_src(1, nx ? tc + 1 : tc), fill_src(0, i + 2 < n_g ? tc + 2 : tc)};
+          char* const dst[2] = {wvtile(V1{}), wktile(K2{})};
+          qk_fills(wktile(K0{}), sc, fs, dst, 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (nx) bias_of(tile_of(i + 1));
+        rescale(bias_max(P % 2, tile_of(i), sc));
+        {
+          bf16x8 pf[4];
+          float lsum = softmax_part(sc, 0, pf);
+          pv_part(wvtile(V0{}), pf, 0);
+          lsum += softmax_part(sc, 1, pf);
+          pv_part(wvtile(V0{}), pf, 1);
+          l_run += lsum;
+        }
+        if (nx) store_bias((P + 1) % 2);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
+    };
+    for (int i = 0; i < n_iter; i += 4) {
+      iterw0(I0{}, i);
+      if (i + 1 < n_iter) iterw0(I1{}, i + 1);
+      if (i + 2 < n_iter) iterw0(I2{}, i + 2);
+      if (i + 3 < n_iter) iterw0(I3{}, i + 3);
+    }
+  } else {
+    if (n_g > 0) qk(wktile(I0{}), sc);
+    auto iterw1 = [&](auto par, int i) {
+      constexpr int P = decltype(par)::value;  // i % 4
+      using V0 = std::integral_constant<int, P % 2>;
+      using K1 = std::integral_constant<int, (P + 1) % 4>;
+      if (i < n_g) {
+        rescale(bias_max(P % 2, tile_of(i), sc));
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          bf16x8 pf[4];
+          float lsum = softmax_part(sc, 0, pf);
+          pv_part(wvtile(V0{}), pf, 0);
+          lsum += softmax_part(sc, 1, pf);
+          pv_part(wvtile(V0{}), pf, 1);
+          qk(wktile(K1{}), sc);
+          l_run += lsum;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
+    };
+    for (int i = 0; i < n_iter; i += 4) {
+      iterw1(I0{}, i);
+      if (i + 1 < n_iter) iterw1(I1{}, i + 1);
+      if (i + 2 < n_iter) iterw1(I2{}, i + 2);
+      if (i + 3 < n_iter) iterw1(I3{}, i + 3);
+    }
+  }
+  // Each wave owns whole rows: normalise and store (lanes l and l + 32 hold the two
+  // halves of each 8-element run, as in the merged store below).
+  const float l_tot = pair_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  const bool o_ok = q_row < Sq && q_row >= q_lo;
+  __bf16* op = a.o + o_boff + row_off_t<kChunked>(a.ov, o_ok ? q_row : 0) + h * a.ov.hs;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      bf16x4 w0, w1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w0[e] = (__bf16)(acc_o[db][8 * k + e] * inv);
+        w1[e] = (__bf16)(acc_o[db][8 * k + 4 + e] * inv);
+      }
+      const uint2 x = __builtin_bit_cast(uint2, w0), y = __builtin_bit_cast(uint2, w1);
+      const auto s0 = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
+      const uint4 out = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+      if (o_ok) *reinterpret_cast<uint4*>(op + db * 32 + 8 * (2 * k + hi)) = out;
+    }
+  return;
   }
 
   // ---- merge the two groups' softmax states through LDS (reusing the K tile
@@ -1130,6 +1280,28 @@ View chunked_view(int64_t B, int64_t L, int64_t H, int64_t hs, int64_t rs) {
   return v;
 }
 
+// Heads of a call to run in 256-row blocks (the rest run in 128-row blocks): the
+// split of the H heads between the two launches that takes the fewest rounds of
+// `cus` workgroups, a round of 256-row blocks counted as 1.9 rounds of 128-row
+// blocks (twice the work in the same cycles per tile, at a clock about 4% higher
+// under the power limit for the halved L2 -> LDS traffic per flop; measured on the
+// video share).  0 unless the split beats 128-row blocks alone.
+int64_t wide_heads(int64_t B, int64_t Sq, int64_t H, int64_t cus) {
+  constexpr double kWideRound = 1.9;
+  const int64_t m128 = (Sq + 127) / 128, m256 = (Sq + 255) / 256;
+  auto rounds = [&](int64_t n) { return double((n + cus - 1) / cus); };
+  double best = rounds(B * H * m128);
+  int64_t best_x = 0;
+  for (int64_t x = 1; x <= H; ++x) {
+    const double t = kWideRound * rounds(B * x * m256) + rounds(B * (H - x) * m128);
+    if (t < best - 0.05) {
+      best = t;
+      best_x = x;
+    }
+  }
+  return best_x;
+}
+
 // Split plan and launch.  Every argument has been validated; ext_* are the byte
 // extents of the operands, for the workspace overlap check.
 int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* v, const View& kv,
@@ -1204,9 +1376,7 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
     }
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // combine: BM * D / 4 threads of 256 per query block
-  const dim3 grid{unsigned(n_work * args.nsplit + (cu_q ? H * B : 0))}, block{unsigned(kThreads)}, cblock{256u},
-      cgrid{unsigned(n_work * (D / 8))};
+  const dim3 block{unsigned(kThreads)};
   // The chunked variants address rows through the views at run time (a view that
   // is not chunked is plain there too).  Segment 1 takes a view of its own when it
   // is chunked or its row stride differs from segment 0's.
@@ -1217,6 +1387,51 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
                    ((kv.chunked && kv.L.d % 64 != 0) || (seg1 && args.kv1.chunked && args.kv1.L.d % 64 != 0)
                         ? kModeCross : 0) |
                    (seg1_rows ? kModeSeg1Rows : 0) | (cu_q ? kModeVarlen : 0) | (args.nsplit > 1 ? kModeSplit : 0);
+  // Calls without packed documents, split-KV or partial outputs (D = 128): heads
+  // [0, wh) run in 256-row blocks (one launch), the rest below in 128-row blocks.
+  if (D == 128 && !cu_q && args.nsplit == 1 && !o_part && !st_o) {
+    const int64_t wh = wide_heads(B, Sq, H, num_cus());
+    if (wh > 0) {
+      AttnArgs w = args;
+      w.H = int(wh);
+      w.m_tiles = int((Sq + 2 * bm - 1) / (2 * bm));
+      w.n_work = int(B * wh * w.m_tiles);
+      w.n_iter_blk = int(n_tiles);  // both groups take every tile
+      const dim3 wgrid{unsigned(w.n_work)};
+      auto launch_w = [&](auto kern) { hipLaunchKernelGGL(kern, wgrid, block, 0, s, w); };
+      switch (mode) {
+        case 0: launch_w(attn_fwd_kernel<128, kModeWide>); break;
+        case kModeChunked: launch_w(attn_fwd_kernel<128, kModeWide + kModeChunked>); break;
+        case kModeChunked + kModeCross: launch_w(attn_fwd_kernel<128, kModeWide + kModeChunked + kModeCross>); break;
+        case kModeTwoSeg: launch_w(attn_fwd_kernel<128, kModeWide + kModeTwoSeg>); break;
+        case kModeTwoSeg + kModeSeg1Rows:
+          launch_w(attn_fwd_kernel<128, kModeWide + kModeTwoSeg + kModeSeg1Rows>);
+          break;
+        case kModeChunked + kModeTwoSeg + kModeSeg1Rows:
+          launch_w(attn_fwd_kernel<128, kModeWide + kModeChunked + kModeTwoSeg + kModeSeg1Rows>);
+          break;
+        case kModeChunked + kModeTwoSeg + kModeCross + kModeSeg1Rows:
+          launch_w(attn_fwd_kernel<128, kModeWide + kModeChunked + kModeTwoSeg + kModeCross + kModeSeg1Rows>);
+          break;
+        default: return CP_ERR_UNSUPPORTED;
+      }
+      if (wh == H) return hip_status(hipGetLastError());
+      args.q += wh * qv.hs;
+      args.k += wh * kv.hs;
+      args.v += wh * kv.hs;
+      args.o += wh * ov.hs;
+      if (seg1) {
+        args.k1 += wh * args.kv1.hs;
+        args.v1 += wh * args.kv1.hs;
+      }
+      args.H = int(H - wh);
+      args.n_work = int(B * (H - wh) * m_tiles);
+    }
+  }
+  // combine: BM * D / 4 threads of 256 per query block
+  const int64_t n_blocks = args.n_work;
+  const dim3 grid{unsigned(n_blocks * args.nsplit + (cu_q ? H * B : 0))}, cblock{256u},
+      cgrid{unsigned(n_blocks * (D / 8))};
   auto launch_fwd = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, args); };
   if (D == 128) {
     if (mode == 0) launch_fwd(attn_fwd_kernel<128, 0>);

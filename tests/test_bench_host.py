@@ -101,3 +101,39 @@ def test_trace_summary_reports_the_attention_kernel(tmp_path):
     flops = workloads.WORKLOADS["image_cp4"].attn_flops_dense()
     tf = flops / 60e-6 / 1e12
     assert f"{tf:.1f} TFLOP/s = {100.0 * tf / 2500.0:.1f}% of the 2.5 PFLOP/s" in text
+
+
+def test_trace_summary_sums_the_launches_of_one_call(tmp_path):
+    # a call that runs its heads in two launches (256-row and 128-row blocks)
+    db = str(tmp_path / "kt2.db")
+    con = sqlite3.connect(db)
+    con.execute("create table top_kernels (name text, total_calls int, total_duration real, average real, "
+                "percentage real)")
+    con.executemany("insert into top_kernels values (?, ?, ?, ?, ?)", [
+        ("void cpattn::(anonymous namespace)::attn_fwd_kernel<128, 64>(cpattn::AttnArgs)", 4, 3600.0, 900.0, 60.0),
+        ("void cpattn::(anonymous namespace)::attn_fwd_kernel<128, 0>(cpattn::AttnArgs)", 4, 1800.0, 450.0, 30.0),
+    ])
+    con.commit()
+    con.close()
+    out = str(tmp_path / "kt2.md")
+    bench.summarize_trace(db, out, "cmd", "video_u2a2")
+    text = open(out).read()
+    tf = workloads.WORKLOADS["video_u2a2"].attn_flops_dense() / 1350e-6 / 1e12
+    assert "/ 1350.00 us" in text and f"{tf:.1f} TFLOP/s" in text
+
+
+def test_traffic_sums_the_launches_of_one_call(tmp_path):
+    fetch, write = str(tmp_path / "fetch"), str(tmp_path / "write")
+    kib = bench.CALIB_BYTES / 1024.0
+    _counter_csv(os.path.join(fetch, "copy"), [("copyBuffer", "FETCH_SIZE", kib)])
+    _counter_csv(os.path.join(write, "copy"), [("copyBuffer", "WRITE_SIZE", kib)])
+    _counter_csv(os.path.join(fetch, "attn"), [("attn_fwd_kernel<128, 64>", "FETCH_SIZE", 300.0),
+                                               ("attn_fwd_kernel<128, 0>", "FETCH_SIZE", 100.0),
+                                               ("attn_fwd_kernel<128, 64>", "FETCH_SIZE", 500.0),
+                                               ("attn_fwd_kernel<128, 0>", "FETCH_SIZE", 100.0)])
+    _counter_csv(os.path.join(write, "attn"), [("attn_fwd_kernel<128, 64>", "WRITE_SIZE", 10.0),
+                                               ("attn_fwd_kernel<128, 0>", "WRITE_SIZE", 20.0)])
+    out = str(tmp_path / "traffic2.json")
+    bench.summarize_traffic(fetch, write, out, "video_u2a2")
+    res = json.load(open(out))
+    assert res["traffic_bytes"] == pytest.approx((400.0 + 100.0 + 30.0) * 1024.0)

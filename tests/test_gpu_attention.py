@@ -120,6 +120,31 @@ def test_scores_rising_past_the_running_max(gu, D, big_half, mask_first):
     _assert_close(got, ref, f"rising D{D} h{big_half} m{int(mask_first)}")
 
 
+@pytest.mark.parametrize("B,H,Sq,Skv,masked", [
+    (1, 64, 1024, 333, False),   # every head in 256-row blocks, ragged key tail
+    (2, 32, 1000, 65, True),     # last block 232 rows (group 1 partly empty), two key tiles, masked
+    (1, 64, 900, 1, False),      # last block 132 rows, one key
+    (1, 64, 1152, 64, True),     # last block 128 rows (group 1 empty), exactly one key tile
+    (1, 6, 16380, 300, False),   # heads 0-3 in 256-row blocks, heads 4-5 in 128-row blocks
+])
+def test_wide_blocks_match_oracle(gu, B, H, Sq, Skv, masked):
+    """Shapes with enough query blocks that a 256-CU part runs some or all heads in
+    256-row blocks (two key groups on different rows sharing every K/V tile)."""
+    D = 128
+    seed = 7000 + Sq + Skv + H
+    q = _rand_bits((B, Sq, H, D), seed)
+    k = _rand_bits((B, Skv, H, D), seed + 1)
+    v = _rand_bits((B, Skv, H, D), seed + 2)
+    mask = None
+    if masked:
+        mask = (np.random.default_rng(seed + 3).random((B, Skv)) > 0.3).astype(np.uint8)
+        mask[:, -1] = 1
+    print(f"[attn] wide B={B} H={H} Sq={Sq} Skv={Skv} masked={masked}", flush=True)
+    got = _run(gu, q, k, v, mask)
+    ref = OA.attention(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), mask)
+    _assert_close(got, ref, f"wide B{B} H{H} Sq{Sq} Skv{Skv} m{int(masked)}")
+
+
 def test_mask_closed_forms(gu):
     B, Sq, Skv, H, D = 3, 70, 150, 2, 128
     q = _rand_bits((B, Sq, H, D), 51)

@@ -126,6 +126,7 @@ def test_scores_rising_past_the_running_max(gu, D, big_half, mask_first):
     (1, 64, 900, 1, False),      # last block 132 rows, one key
     (1, 64, 1152, 64, True),     # last block 128 rows (group 1 empty), exactly one key tile
     (1, 6, 16380, 300, False),   # heads 0-3 in 256-row blocks, heads 4-5 in 128-row blocks
+    (2, 6, 8192, 100, True),     # the same split with two batches
 ])
 def test_wide_blocks_match_oracle(gu, B, H, Sq, Skv, masked):
     """Shapes with enough query blocks that a 256-CU part runs some or all heads in
@@ -271,6 +272,7 @@ def _fused_ref_chain(cp, recv_d, B, W, md):
     (2, 4, 40, 2, 128, True),     # chunks shorter than a tile: a tile spans up to three chunks
     (2, 3, 8, 1, 64, True),       # eight-row chunks
     (2, 2, 1000, 1, 128, False),  # 32 query blocks with spanning tiles: split-KV
+    (2, 2, 1000, 16, 128, True),  # 256 blocks of 256 rows: wide blocks over chunks that tiles span
 ])
 def test_recv_to_send_matches_oracle_and_unfused(gu, B, W, Sl, Hl, D, masked):
     import context_attention_diffusion_amd as cp
@@ -300,6 +302,7 @@ def test_recv_to_send_matches_oracle_and_unfused(gu, B, W, Sl, Hl, D, masked):
     (2, 2, 64, 3, 128, 128, False, True),    # several batches: chunked received rows
     (2, 3, 70, 1, 64, 210, True, True),      # chunked rows whose tiles span chunks, two segments
     (1, 4, 512, 1, 128, 2048, False, False), # split-KV
+    (2, 2, 1000, 16, 128, 500, True, True),  # wide blocks: chunked rows, spanning tiles, two segments
 ])
 def test_recv_to_send_2d_matches_oracle_and_unfused(gu, B, W, Sl, Hl, D, So, other_first, masked):
     import context_attention_diffusion_amd as cp

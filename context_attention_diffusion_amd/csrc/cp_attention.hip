@@ -832,8 +832,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // the fills of V tile i + 1 and K tile i + 2 between its steps, then the max,
   // softmax and P V (V buffer i % 2); group 1 takes the max, softmax and P V of
   // tile i (scores from the previous iteration), then Q K^T of tile i + 1.  During
-  // iteration i the buffers being filled held V tile i - 1 and K tile i - 2, whose
-  // last reads were in iteration i - 1.  Group 0 issues every fill and writes the
+  // iteration i the buffers being filled held V tile i - 1 and K tile i - 2, last
+  // read no later than iteration i - 1.  Group 0 issues every fill and writes the
   // bias rows (tile i in slot i % 2), which both groups read in iteration i.
   if (grp == 0) {
     if (n_g > 0) {

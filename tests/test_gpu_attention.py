@@ -223,6 +223,8 @@ def test_full_size_workloads_whole(gu, name):
     (2, 3, 70, 700, 64, True),       # masked, ragged keys, D 64
     (1, 1, 5, 3000, 128, True),      # one query block split many ways, most rows invalid
     (1, 24, 1088, 4352, 128, False),  # image CP4 share: 216 blocks, split over the compute units
+    (1, 24, 512, 2600, 128, False),  # image CP8 rows, ragged keys: 96 blocks, each split over 2 workgroups
+    (2, 12, 512, 2600, 128, True),   # the same with two batches and a key mask
 ])
 def test_split_kv_matches_oracle_and_unsplit(gu, B, H, Sq, Skv, D, masked):
     import context_attention_diffusion_amd as cp

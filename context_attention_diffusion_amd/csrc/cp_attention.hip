@@ -1292,7 +1292,8 @@ int64_t wide_heads(int64_t B, int64_t Sq, int64_t H, int64_t cus) {
   auto rounds = [&](int64_t n) { return double((n + cus - 1) / cus); };
   double best = rounds(B * H * m128);
   int64_t best_x = 0;
-  for (int64_t x = 1; x <= H; ++x) {
+  // (every split for up to 4096 heads; beyond that only all heads in 256-row blocks)
+  for (int64_t x = H <= 4096 ? 1 : H; x <= H; ++x) {
     const double t = kWideRound * rounds(B * x * m256) + rounds(B * (H - x) * m128);
     if (t < best - 0.05) {
       best = t;

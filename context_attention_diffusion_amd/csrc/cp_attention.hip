@@ -248,9 +248,13 @@ struct AttnArgs {
   float* ws;           // partial states, slot = query block * nsplit + part:
                        // O [n_work * nsplit][BM][D] fp32, then (m, l) [n_work * nsplit][BM][2]
   // Partial-attention output (instead of o): normalised O [B][Sq][H][D] fp32 and
-  // lse = ln(sum of exp(scale q.k) over the valid keys) [B][H][Sq] fp32.
+  // lse = ln(sum of exp(scale q.k) over the valid keys) [B][H][Sq] fp32, over all
+  // H_all heads of the call; this launch's head h is head h_base + h there (a call
+  // may split its heads between two launches).
   float* o_part;
   float* lse;
+  int H_all;
+  int h_base;
   // Running state of an attention over earlier key chunks (same format as
   // o_part / lse), folded into this call's result; NULL: none.
   const float* st_o;
@@ -704,6 +708,89 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     s[1] = acc1;
   };
 
+  // Partial output of this wave's rows: the call's normalised output and lse over
+  // its keys, folded into the running state when there is one: L = ln(e^lse_s +
+  // e^lse_k), O = e^(lse_s - L) O_s + e^(lse_k - L) O_k.  Output: fp32 O and L
+  // (o_part, lse), or bf16 O (o).  The state is acc_o scaled by c0, plus (merged:
+  // the 128-row block) the other group's accumulators cb scaled by c1; mm and l_tot
+  // are its max and row sum, in the kernel's log2 units.
+  float4 cb[C::DB][4];  // the other group's O (128-row block, group 0 after the merge)
+  auto emit_partial = [&](auto merged, float mm, float l_tot, float c0, float c1) {
+    constexpr bool kMerged = decltype(merged)::value;
+    if (q_row >= a.Sq) return;
+    const int hh = a.h_base + h;
+    const size_t orow = ((size_t(b) * a.Sq + q_row) * a.H_all + hh) * D;
+    const size_t lidx = (size_t(b) * a.H_all + hh) * a.Sq + q_row;
+    // sum_j e^{z_j} = 2^mm * l_tot
+    const float lse_k = l_tot > 0.f ? (mm + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    float L = lse_k, wk = 1.f, ws = 0.f;
+    const float* sp = nullptr;
+    if (a.st_o != nullptr) {
+      const float lse_s = a.st_lse[lidx];
+      if (lse_s != -INFINITY) {
+        sp = a.st_o + orow;
+        if (lse_k == -INFINITY) {
+          L = lse_s;
+          ws = 1.f;
+          wk = 0.f;
+        } else {
+          L = fmaxf(lse_s, lse_k) + log1pf(expf(-fabsf(lse_s - lse_k)));
+          ws = expf(lse_s - L);
+          wk = expf(lse_k - L);
+        }
+      }
+    }
+    const float k0 = c0 * wk, k1 = c1 * wk;
+    float4 out[C::DB][4];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4 w;
+        w.x = acc_o[db][4 * g + 0] * k0;
+        w.y = acc_o[db][4 * g + 1] * k0;
+        w.z = acc_o[db][4 * g + 2] * k0;
+        w.w = acc_o[db][4 * g + 3] * k0;
+        if constexpr (kMerged) {
+          w.x += cb[db][g].x * k1;
+          w.y += cb[db][g].y * k1;
+          w.z += cb[db][g].z * k1;
+          w.w += cb[db][g].w * k1;
+        } else {
+          (void)k1;
+        }
+        if (sp != nullptr) {
+          const float4 sv = *reinterpret_cast<const float4*>(sp + db * 32 + 8 * g + 4 * hi);
+          w.x += ws * sv.x;
+          w.y += ws * sv.y;
+          w.z += ws * sv.z;
+          w.w += ws * sv.w;
+        }
+        out[db][g] = w;
+      }
+    if (a.o_part != nullptr) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(a.o_part + orow + db * 32 + 8 * g + 4 * hi) = out[db][g];
+      if (hi == 0) a.lse[lidx] = L;
+    } else {
+      __bf16* op = a.o + b * a.ov.bs + row_off_t<kChunked>(a.ov, q_row) + h * a.ov.hs;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 w;
+          w[0] = (__bf16)out[db][g].x;
+          w[1] = (__bf16)out[db][g].y;
+          w[2] = (__bf16)out[db][g].z;
+          w[3] = (__bf16)out[db][g].w;
+          *reinterpret_cast<bf16x4*>(op + db * 32 + 8 * g + 4 * hi) = w;
+        }
+    }
+  };
+
   if constexpr (!kWide) {
   // ---- prologue.  Group 0 consumes K and V of tile i in iteration i; group 1
   // runs one K tile ahead (its iteration i ends with the scores of tile i+1, whose
@@ -921,6 +1008,10 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // halves of each 8-element run, as in the merged store below).
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (a.o_part != nullptr || a.st_o != nullptr) {
+    emit_partial(std::false_type{}, m_run, l_tot, inv, 0.f);
+    return;
+  }
   const bool o_ok = q_row < Sq && q_row >= q_lo;
   __bf16* op = a.o + o_boff + row_off_t<kChunked>(a.ov, o_ok ? q_row : 0) + h * a.ov.hs;
 #pragma unroll
@@ -962,7 +1053,6 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   }
   __syncthreads();
   if (grp == 0) {
-    float4 cb[C::DB][4];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -998,73 +1088,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const float c0 = a0 * inv, c1 = a1 * inv;
     if (a.o_part != nullptr || a.st_o != nullptr) {
-      // This call's normalised output and lse over its keys, folded into the running
-      // state when there is one: L = ln(e^lse_s + e^lse_k), O = e^(lse_s - L) O_s +
-      // e^(lse_k - L) O_k.  Output: fp32 O and L (o_part, lse), or bf16 O (o).
-      if (q_row < a.Sq) {
-        const size_t orow = ((size_t(b) * a.Sq + q_row) * a.H + h) * D;
-        const size_t lidx = (size_t(b) * a.H + h) * a.Sq + q_row;
-        // sum_j e^{z_j} = 2^mm * l_tot, with mm and l_tot in the kernel's log2 units
-        const float lse_k = l_tot > 0.f ? (mm + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-        float L = lse_k, wk = 1.f, ws = 0.f;
-        const float* sp = nullptr;
-        if (a.st_o != nullptr) {
-          const float lse_s = a.st_lse[lidx];
-          if (lse_s != -INFINITY) {
-            sp = a.st_o + orow;
-            if (lse_k == -INFINITY) {
-              L = lse_s;
-              ws = 1.f;
-              wk = 0.f;
-            } else {
-              L = fmaxf(lse_s, lse_k) + log1pf(expf(-fabsf(lse_s - lse_k)));
-              ws = expf(lse_s - L);
-              wk = expf(lse_k - L);
-            }
-          }
-        }
-        const float k0 = c0 * wk, k1 = c1 * wk;
-        float4 out[C::DB][4];
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float4 w;
-            w.x = acc_o[db][4 * g + 0] * k0 + cb[db][g].x * k1;
-            w.y = acc_o[db][4 * g + 1] * k0 + cb[db][g].y * k1;
-            w.z = acc_o[db][4 * g + 2] * k0 + cb[db][g].z * k1;
-            w.w = acc_o[db][4 * g + 3] * k0 + cb[db][g].w * k1;
-            if (sp != nullptr) {
-              const float4 sv = *reinterpret_cast<const float4*>(sp + db * 32 + 8 * g + 4 * hi);
-              w.x += ws * sv.x;
-              w.y += ws * sv.y;
-              w.z += ws * sv.z;
-              w.w += ws * sv.w;
-            }
-            out[db][g] = w;
-          }
-        if (a.o_part != nullptr) {
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-              *reinterpret_cast<float4*>(a.o_part + orow + db * 32 + 8 * g + 4 * hi) = out[db][g];
-          if (hi == 0) a.lse[lidx] = L;
-        } else {
-          __bf16* op = a.o + b * a.ov.bs + row_off_t<kChunked>(a.ov, q_row) + h * a.ov.hs;
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              bf16x4 w;
-              w[0] = (__bf16)out[db][g].x;
-              w[1] = (__bf16)out[db][g].y;
-              w[2] = (__bf16)out[db][g].z;
-              w[3] = (__bf16)out[db][g].w;
-              *reinterpret_cast<bf16x4*>(op + db * 32 + 8 * g + 4 * hi) = w;
-            }
-        }
-      }
+      emit_partial(std::true_type{}, mm, l_tot, c0, c1);
       return;
     }
     // Accumulator row r of block db is d = db*32 + 8*(r/4) + 4*hi + r%4: lanes l and
@@ -1352,6 +1376,8 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
   args.ws = nullptr;
   args.o_part = o_part;
   args.lse = lse;
+  args.H_all = int(H);
+  args.h_base = 0;
   args.st_o = st_o;
   args.st_lse = st_lse;
   args.cu_q = cu_q;
@@ -1388,9 +1414,9 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
                    ((kv.chunked && kv.L.d % 64 != 0) || (seg1 && args.kv1.chunked && args.kv1.L.d % 64 != 0)
                         ? kModeCross : 0) |
                    (seg1_rows ? kModeSeg1Rows : 0) | (cu_q ? kModeVarlen : 0) | (args.nsplit > 1 ? kModeSplit : 0);
-  // Calls without packed documents, split-KV or partial outputs (D = 128): heads
-  // [0, wh) run in 256-row blocks (one launch), the rest below in 128-row blocks.
-  if (D == 128 && !cu_q && args.nsplit == 1 && !o_part && !st_o) {
+  // Calls without packed documents or split-KV (D = 128): heads [0, wh) run in
+  // 256-row blocks (one launch), the rest below in 128-row blocks.
+  if (D == 128 && !cu_q && args.nsplit == 1) {
     const int64_t wh = wide_heads(B, Sq, H, num_cus());
     if (wh > 0) {
       AttnArgs w = args;
@@ -1420,7 +1446,8 @@ int attn_launch(const __bf16* q, const View& qv, const __bf16* k, const __bf16* 
       args.q += wh * qv.hs;
       args.k += wh * kv.hs;
       args.v += wh * kv.hs;
-      args.o += wh * ov.hs;
+      if (args.o) args.o += wh * ov.hs;
+      args.h_base = int(wh);  // partial outputs index the call's heads
       if (seg1) {
         args.k1 += wh * args.kv1.hs;
         args.v1 += wh * args.kv1.hs;

@@ -422,6 +422,8 @@ def _partials(cp, qd, k, v, mask, edges):
     (2, 3, 70, 300, 64, (64,), True),
     (1, 1, 5, 200, 128, (1, 2, 150), True),
     (2, 2, 257, 700, 128, (350,), False),
+    (1, 64, 1000, 700, 128, (333,), True),     # every head in 256-row blocks, ragged last block
+    (2, 6, 8192, 260, 128, (100,), False),     # heads 0-3 in 256-row blocks, heads 4-5 in 128-row blocks
 ])
 def test_partial_and_merge_match_oracle(gu, B, H, Sq, Skv, D, cuts, masked):
     import context_attention_diffusion_amd as cp
@@ -547,6 +549,8 @@ def test_joint_cfg_workload_segments(gu):
     (1, 2, 130, 1133, 128, (100, 433), False),
     (2, 3, 70, 300, 64, (64, 65), True),
     (2, 2, 257, 700, 128, (350,), True),
+    (1, 64, 1000, 500, 128, (100, 300), True),  # every head in 256-row blocks
+    (1, 6, 16380, 300, 128, (64, 200), False),  # heads split between 256- and 128-row blocks
 ])
 def test_partial_accumulate_matches_oracle(gu, B, H, Sq, Skv, D, cuts, masked):
     """partial(chunk 0) -> accumulate in place (middle chunks) -> accumulate with final

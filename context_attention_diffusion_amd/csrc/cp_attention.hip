@@ -67,7 +67,8 @@
 // boundaries read from device memory); 32 = split-KV (the key range of each
 // query block cut over nsplit workgroups, whose partial states a separate
 // kernel merges); 64 = wide blocks (with 0, 1, 5, 2, 10, 11 and 15).  The
-// partial / accumulating outputs are run-time paths.
+// partial / accumulating outputs are run-time paths of the 128-row and wide
+// blocks alike.
 
 #include <hip/hip_runtime.h>
 
@@ -287,7 +288,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // Wide block: 256 query rows, group g on rows [128 g, 128 g + 128), both groups on
   // every key tile (group 1 one Q K^T ahead, as in the 128-row block), so each K/V
   // tile brought into LDS serves twice the rows.  Not for packed documents or
-  // split-KV parts, and the output is always bf16 O.
+  // split-KV parts; each wave writes its own rows (bf16 O, or the partial output).
   constexpr bool kWide = (MODE & kModeWide) != 0;
   static_assert(!kWide || (!kVarlen && !kSplit), "the wide block has no packed-document or split-KV form");
   using C = Cfg<D>;

@@ -389,6 +389,11 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 
   // ---- Q fragment (B operand of S^T = K Q^T): query row q_row, d = ks*16 + 8*hi .. +8
   const int q_row = mt * BMB + (kWide ? grp * C::BM : 0) + gw * 32 + l32;
+  // A wave whose 32 rows all lie past the last query row (the last block of a
+  // head when Sq is not a multiple of the block) only issues its share of the
+  // fills and bias rows and meets every barrier: its MFMA and softmax work would
+  // go to rows that are never stored.
+  const bool idle = !kVarlen && __builtin_amdgcn_readfirstlane(q_row - l32) >= Sq;
   bf16x8 qf[C::KS];
   {
     const bool ok = q_row < Sq && q_row >= q_lo;
@@ -830,7 +835,35 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // is in its Q K^T MFMAs while group 1 is in its softmax VALU work, then the
   // roles swap, so the matrix pipe and the VALU overlap across the two waves.
   // Iterations come in pairs so that every buffer choice is compile-time.
-  if (grp == 0) {
+  if (grp == 0 && idle) {
+    // the fills and bias rows of iter0 below, without its MFMA and softmax work
+    auto iter0_idle = [&](auto par, int i) {
+      constexpr int P = decltype(par)::value;
+      using BP = std::integral_constant<int, P>;
+      using BQ = std::integral_constant<int, 1 - P>;
+      if (i < n_g) {
+        const bool nx = i + 1 < n_g;
+        const bool want[4] = {nx, nx, i + 2 < n_g1, i + 1 < n_g1};
+        const int tc = 2 * (i0 + i);
+        const int tl[4] = {want[0] ? 2 * (i0 + i + 1) : tc, want[1] ? 2 * (i0 + i + 1) : tc,
+                           want[2] ? 2 * (i0 + i + 2) + 1 : tc, want[3] ? 2 * (i0 + i + 1) + 1 : tc};
+        const FillSrc fs[4] = {fill_src(1, tl[3]), fill_src(0, tl[0]), fill_src(1, tl[1]), fill_src(0, tl[2])};
+        char* const dst[4] = {vtile(I1{}, BQ{}), ktile(I0{}, BQ{}), vtile(I0{}, BQ{}), ktile(I1{}, BP{})};
+#pragma unroll
+        for (int f = 0; f < 4 * C::SPT; ++f) fill_one(fs[f / C::SPT], f % C::SPT, dst[f / C::SPT]);
+        if (nx) {
+          bias_of(tile_of(i + 1));
+          store_bias(1 - P);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
+    };
+    for (int i = 0; i < n_iter; i += 2) {
+      iter0_idle(I0{}, i);
+      if (i + 1 < n_iter) iter0_idle(I1{}, i + 1);
+    }
+  } else if (grp == 0) {
     auto iter0 = [&](auto par, int i) {
       constexpr int P = decltype(par)::value;
       using BP = std::integral_constant<int, P>;
@@ -873,6 +906,16 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     for (int i = 0; i < n_iter; i += 2) {
       iter0(I0{}, i);
       if (i + 1 < n_iter) iter0(I1{}, i + 1);
+    }
+  } else if (idle) {
+    // the bias rows of iter1 below, without its MFMA and softmax work
+    for (int i = 0; i < n_iter; ++i) {
+      if (i < n_g && i + 3 < n_g) {
+        bias_of(tile_of(i + 3));
+        store_bias((i + 3) & 3);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
     }
   } else {
     if (n_g > 0) {
@@ -936,7 +979,29 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   __syncthreads();
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  if (grp == 0) {
+  if (grp == 0 && idle) {
+    // the fills and bias rows of iterw0 below, without its MFMA and softmax work
+    for (int i = 0; i < n_iter; ++i) {
+      if (i < n_g) {
+        const bool nx = i + 1 < n_g;
+        const int tc = tile_of(i);
+        const FillSrc fv = fill_src(1, nx ? tc + 1 : tc), fk = fill_src(0, i + 2 < n_g ? tc + 2 : tc);
+        char* const dv = (i & 1) ? wvtile(I0{}) : wvtile(I1{});
+        char* const dk = (i & 3) == 0 ? wktile(I2{}) : (i & 3) == 1 ? wktile(I3{}) : (i & 3) == 2 ? wktile(I0{})
+                                                                                                  : wktile(I1{});
+#pragma unroll
+        for (int j = 0; j < C::SPT; ++j) fill_one(fv, j, dv);
+#pragma unroll
+        for (int j = 0; j < C::SPT; ++j) fill_one(fk, j, dk);
+        if (nx) {
+          bias_of(tile_of(i + 1));
+          store_bias((i + 1) & 1);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
+    }
+  } else if (grp == 0) {
     auto iterw0 = [&](auto par, int i) {
       constexpr int P = decltype(par)::value;  // i % 4
       using V0 = std::integral_constant<int, P % 2>;
@@ -974,6 +1039,11 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       if (i + 1 < n_iter) iterw0(I1{}, i + 1);
       if (i + 2 < n_iter) iterw0(I2{}, i + 2);
       if (i + 3 < n_iter) iterw0(I3{}, i + 3);
+    }
+  } else if (idle) {
+    for (int i = 0; i < n_iter; ++i) {
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
     }
   } else {
     if (n_g > 0) qk(wktile(I0{}), sc);

@@ -125,6 +125,7 @@ def test_scores_rising_past_the_running_max(gu, D, big_half, mask_first):
     (2, 32, 1000, 65, True),     # last block 232 rows (group 1 partly empty), two key tiles, masked
     (1, 64, 900, 1, False),      # last block 132 rows, one key
     (1, 64, 1152, 64, True),     # last block 128 rows (group 1 empty), exactly one key tile
+    (1, 64, 800, 333, True),     # last block 32 rows: waves 1-3 of group 0 and all of group 1 idle, six tiles
     (1, 6, 16380, 300, False),   # heads 0-3 in 256-row blocks, heads 4-5 in 128-row blocks
     (2, 6, 8192, 100, True),     # the same split with two batches
 ])

@@ -550,24 +550,36 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // (wide block: one row per tile, slot i % 2, written by group 0 and read by both)
   float* bias_row = lds2_bias + (kWide ? 0 : grp * 2 * C::BN);
 
-  // Key validity of tile t as an additive bias, one key per thread of wave 0.
-  // The mask byte is loaded here and only compared when the bias row is
-  // stored, late in the iteration, so its load latency is never waited on early.
+  // Key validity of tile t as an additive bias, one key per lane.  The mask byte
+  // is loaded here and only compared when the bias row is stored, late in the
+  // iteration, so its load latency is never waited on early.  Wave 0 of the
+  // group writes the row; with a mask every wave also keeps, per bias slot, a bit
+  // that says whether the tile has an invalid key (mflags), so that a tile whose
+  // keys are all valid skips the bias (most tiles of a padding mask).
+  const bool has_mask = mbase != nullptr || mbase1 != nullptr;
   bool kvalid = true;
   uint32_t mraw = 1;
+  uint32_t mflags = 0;
   auto bias_of = [&](int t) {
-    if (gt < C::BN) {
+    if (gt < C::BN || has_mask) {
       bool s1;
       int key0, len;
       seg_of(t, s1, key0, len);
-      const int key = key0 + gt;
+      const int key = key0 + lane;
       kvalid = key < len;
       const uint8_t* mb = s1 ? mbase1 : mbase;
       mraw = mb ? uint32_t(mb[kvalid ? key : 0]) : 1u;
     }
   };
+  auto note_bias = [&](int buf) {
+    if (has_mask) {
+      const uint32_t bit = 1u << buf;
+      mflags = __builtin_amdgcn_ballot_w64(!(kvalid && mraw != 0)) != 0 ? (mflags | bit) : (mflags & ~bit);
+    }
+  };
   auto store_bias = [&](int buf) {
     if (gt < C::BN) bias_row[buf * C::BN + gt] = (kvalid && mraw != 0) ? 0.f : -INFINITY;
+    note_bias(buf);
   };
 
   // ---- LDS readers
@@ -618,7 +630,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     bool s1;
     int key0, len;
     seg_of(t, s1, key0, len);
-    if ((s1 ? mbase1 : mbase) != nullptr || key0 + C::BN > len) {
+    if (key0 + C::BN > len || ((s1 ? mbase1 : mbase) != nullptr && ((mflags >> buf) & 1u) != 0)) {
       const float* br = bias_row + buf * C::BN;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -974,6 +986,10 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       store_bias(0);
     }
     if (n_g > 1) fill(0, tile_of(1), wktile(I1{}));
+  } else if (has_mask && n_g > 0) {
+    // group 1 keeps its own mask bits (group 0 writes the rows)
+    bias_of(tile_of(0));
+    note_bias(0);
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's LDS fills have landed
   __syncthreads();
@@ -1052,6 +1068,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       using V0 = std::integral_constant<int, P % 2>;
       using K1 = std::integral_constant<int, (P + 1) % 4>;
       if (i < n_g) {
+        const bool nb = has_mask && i + 1 < n_g;
+        if (nb) bias_of(tile_of(i + 1));
         rescale(bias_max(P % 2, tile_of(i), sc));
         __builtin_amdgcn_sched_barrier(0);
         {
@@ -1064,6 +1082,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
           l_run += lsum;
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (nb) note_bias((P + 1) % 2);
       }
       __builtin_amdgcn_s_waitcnt(0x0f70);
       __syncthreads();

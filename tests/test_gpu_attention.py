@@ -147,6 +147,36 @@ def test_wide_blocks_match_oracle(gu, B, H, Sq, Skv, masked):
     _assert_close(got, ref, f"wide B{B} H{H} Sq{Sq} Skv{Skv} m{int(masked)}")
 
 
+@pytest.mark.parametrize("B,H,Sq,Skv,split", [
+    (2, 3, 200, 1000, False),    # 128-row blocks, both key groups
+    (2, 3, 200, 1000, True),     # the same through split-KV
+    (1, 64, 1024, 700, False),   # 256-row blocks (group 1 keeps its own mask bits)
+    (1, 6, 16380, 300, False),   # heads split between 256- and 128-row blocks
+])
+def test_sparse_mask_tiles(gu, B, H, Sq, Skv, split):
+    """Single invalid keys in a few tiles (adjacent ones, the last one, both key
+    groups), every other tile fully valid, and huge values on the invalid keys: a
+    tile that skipped its bias would let one of them into the output."""
+    import context_attention_diffusion_amd as cp
+    D = 128
+    seed = 9100 + Sq + Skv + H
+    q = _rand_bits((B, Sq, H, D), seed)
+    k = _rand_bits((B, Skv, H, D), seed + 1)
+    v = _rand_bits((B, Skv, H, D), seed + 2)
+    mask = np.ones((B, Skv), np.uint8)
+    for b in range(B):
+        for key in (7 + 3 * b, 97 + 3 * b, 188 + b, Skv - 2 - b):
+            mask[b, key] = 0
+            v[b, key] = bf16.f64_to_bits_rne(np.full((H, D), 1000.0))
+    print(f"[attn] sparse mask B={B} H={H} Sq={Sq} Skv={Skv} split={split}", flush=True)
+    qd, kd, vd = gu.to_dev(q), gu.to_dev(k), gu.to_dev(v)
+    md = torch.from_numpy(mask).to(gu.DEV)
+    o = cp.cp_attn_localq_globalkv(qd, kd, vd, md, split=split)
+    torch.cuda.synchronize()
+    ref = OA.attention(bf16.bits_to_f64(q), bf16.bits_to_f64(k), bf16.bits_to_f64(v), mask)
+    _assert_close(gu.to_f64(o), ref, f"sparse mask B{B} H{H} Sq{Sq} Skv{Skv} split{int(split)}")
+
+
 def test_mask_closed_forms(gu):
     B, Sq, Skv, H, D = 3, 70, 150, 2, 128
     q = _rand_bits((B, Sq, H, D), 51)

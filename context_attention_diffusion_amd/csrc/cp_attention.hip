@@ -946,17 +946,16 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
         rescale(bias_max(i & 3, tile_of(i), sc));
         __builtin_amdgcn_sched_barrier(0);
         // tile i's softmax and P V in two halves, then tile i+1's Q K^T as two
-        // interleaved chains (computed unconditionally: on the last tile it reads an
-        // idle buffer and is discarded).  The second half's softmax then runs while
-        // group 0 is in its P V MFMAs, and this group's Q K^T while group 0 waits
-        // for its fills.
+        // interleaved chains (none after the group's last tile).  The second half's
+        // softmax then runs while group 0 is in its P V MFMAs, and this group's
+        // Q K^T while group 0 waits for its fills.
         {
           bf16x8 pf[4];
           float lsum = softmax_part(sc, 0, pf);
           pv_part(vtile(I1{}, BP{}), pf, 0);
           lsum += softmax_part(sc, 1, pf);
           pv_part(vtile(I1{}, BP{}), pf, 1);
-          qk(ktile(I1{}, BQ{}), sc);
+          if (i + 1 < n_g) qk(ktile(I1{}, BQ{}), sc);
           l_run += lsum;
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1028,7 +1027,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
         const bool nx = i + 1 < n_g;
         {
           // past the last tile the current one is re-read into a buffer whose
-          // contents nothing uses (group 1's last Q K^T is discarded)
+          // contents nothing reads before its next fill
           const int tc = tile_of(i);
           const FillSrc fs[2] = {fill_src(1, nx ? tc + 1 : tc), fill_src(0, i + 2 < n_g ? tc + 2 : tc)};
           char* const dst[2] = {wvtile(V1{}), wktile(K2{})};
@@ -1078,7 +1077,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
           pv_part(wvtile(V0{}), pf, 0);
           lsum += softmax_part(sc, 1, pf);
           pv_part(wvtile(V0{}), pf, 1);
-          qk(wktile(K1{}), sc);
+          if (i + 1 < n_g) qk(wktile(K1{}), sc);
           l_run += lsum;
         }
         __builtin_amdgcn_sched_barrier(0);

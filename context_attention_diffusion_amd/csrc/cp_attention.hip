@@ -498,10 +498,19 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     int key0, rows;
     bool seg1, cross;
   };
-  auto fill_src = [&](int which, int t) -> FillSrc {
+  // segc: the segment of tile t when the caller knows it at compile time (0 or 1),
+  // so that the choice of base, view and lane offsets folds away; -1: from t.
+  auto fill_src_in = [&](auto segc, int which, int t) -> FillSrc {
+    constexpr int SG = decltype(segc)::value;
     bool s1;
     int key0, len;
-    seg_of(t, s1, key0, len);
+    if constexpr (kTwoSeg && SG >= 0) {
+      s1 = SG == 1;
+      key0 = (SG == 1 ? t - a.nt0 : t) * C::BN;
+      len = SG == 1 ? a.Skv1 : a.Skv;
+    } else {
+      seg_of(t, s1, key0, len);
+    }
     const int rows = min(C::BN, len - key0);
     // (plain two-segment calls share K/V's row stride: segment 1 only changes the base)
     const View& v = (kSeg1Rows && s1) ? a.kv1 : a.kv;
@@ -511,6 +520,10 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
                                               0x00020000),
             key0, rows, s1, cr};
   };
+  using SegDyn = std::integral_constant<int, -1>;
+  using Seg0 = std::integral_constant<int, 0>;
+  using Seg1 = std::integral_constant<int, 1>;
+  auto fill_src = [&](int which, int t) -> FillSrc { return fill_src_in(SegDyn{}, which, t); };
   // Instruction j of a tile's fill into the tile array dst.
   auto fill_one = [&](const FillSrc& f, int j, char* dst) {
     fill_j(j, f.rs, dst,
@@ -876,7 +889,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       if (i + 1 < n_iter) iter0_idle(I1{}, i + 1);
     }
   } else if (grp == 0) {
-    auto iter0 = [&](auto par, int i) {
+    auto iter0 = [&](auto par, auto segc, int i) {
       constexpr int P = decltype(par)::value;
       using BP = std::integral_constant<int, P>;
       using BQ = std::integral_constant<int, 1 - P>;
@@ -895,7 +908,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
           const int tc = 2 * (i0 + i);
           const int tl[4] = {want[0] ? 2 * (i0 + i + 1) : tc, want[1] ? 2 * (i0 + i + 1) : tc,
                              want[2] ? 2 * (i0 + i + 2) + 1 : tc, want[3] ? 2 * (i0 + i + 1) + 1 : tc};
-          const FillSrc fs[4] = {fill_src(1, tl[3]), fill_src(0, tl[0]), fill_src(1, tl[1]), fill_src(0, tl[2])};
+          const FillSrc fs[4] = {fill_src_in(segc, 1, tl[3]), fill_src_in(segc, 0, tl[0]),
+                                 fill_src_in(segc, 1, tl[1]), fill_src_in(segc, 0, tl[2])};
           char* const dst[4] = {vtile(I1{}, BQ{}), ktile(I0{}, BQ{}), vtile(I0{}, BQ{}), ktile(I1{}, BP{})};
           qk_fills(ktile(I0{}, BP{}), sc, fs, dst, 4);
         }
@@ -915,9 +929,21 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       __builtin_amdgcn_s_waitcnt(0x0f70);
       __syncthreads();
     };
-    for (int i = 0; i < n_iter; i += 2) {
-      iter0(I0{}, i);
-      if (i + 1 < n_iter) iter0(I1{}, i + 1);
+    // Two key segments: the pairs of iterations whose fills (tiles 2(i0+i) ..
+    // 2(i0+i+3)+1) all lie in segment 0, then those that straddle the boundary,
+    // then those in segment 1, each run as a loop of its own with the fills'
+    // segment fixed where it is known.
+    auto pair = [&](auto segc, int i) {
+      iter0(I0{}, segc, i);
+      if (i + 1 < n_iter) iter0(I1{}, segc, i + 1);
+    };
+    int i = 0;
+    if constexpr (kTwoSeg) {
+      for (; i < n_iter && 2 * (i0 + i + 3) + 1 < a.nt0; i += 2) pair(Seg0{}, i);
+      for (; i < n_iter && 2 * (i0 + i) < a.nt0; i += 2) pair(SegDyn{}, i);
+      for (; i < n_iter; i += 2) pair(Seg1{}, i);
+    } else {
+      for (; i < n_iter; i += 2) pair(SegDyn{}, i);
     }
   } else if (idle) {
     // the bias rows of iter1 below, without its MFMA and softmax work
@@ -1017,7 +1043,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       __syncthreads();
     }
   } else if (grp == 0) {
-    auto iterw0 = [&](auto par, int i) {
+    auto iterw0 = [&](auto par, auto segc, int i) {
       constexpr int P = decltype(par)::value;  // i % 4
       using V0 = std::integral_constant<int, P % 2>;
       using V1 = std::integral_constant<int, (P + 1) % 2>;
@@ -1029,7 +1055,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
           // past the last tile the current one is re-read into a buffer whose
           // contents nothing reads before its next fill
           const int tc = tile_of(i);
-          const FillSrc fs[2] = {fill_src(1, nx ? tc + 1 : tc), fill_src(0, i + 2 < n_g ? tc + 2 : tc)};
+          const FillSrc fs[2] = {fill_src_in(segc, 1, nx ? tc + 1 : tc), fill_src_in(segc, 0, i + 2 < n_g ? tc + 2 : tc)};
           char* const dst[2] = {wvtile(V1{}), wktile(K2{})};
           qk_fills(wktile(K0{}), sc, fs, dst, 2);
         }
@@ -1049,11 +1075,22 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       __builtin_amdgcn_s_waitcnt(0x0f70);
       __syncthreads();
     };
-    for (int i = 0; i < n_iter; i += 4) {
-      iterw0(I0{}, i);
-      if (i + 1 < n_iter) iterw0(I1{}, i + 1);
-      if (i + 2 < n_iter) iterw0(I2{}, i + 2);
-      if (i + 3 < n_iter) iterw0(I3{}, i + 3);
+    // (two key segments: runs of four iterations whose fills, tiles i0+i ..
+    // i0+i+5, all lie in segment 0, then those straddling the boundary, then
+    // those in segment 1, as loops of their own)
+    auto quad = [&](auto segc, int i) {
+      iterw0(I0{}, segc, i);
+      if (i + 1 < n_iter) iterw0(I1{}, segc, i + 1);
+      if (i + 2 < n_iter) iterw0(I2{}, segc, i + 2);
+      if (i + 3 < n_iter) iterw0(I3{}, segc, i + 3);
+    };
+    int i = 0;
+    if constexpr (kTwoSeg) {
+      for (; i < n_iter && i0 + i + 5 < a.nt0; i += 4) quad(Seg0{}, i);
+      for (; i < n_iter && i0 + i < a.nt0; i += 4) quad(SegDyn{}, i);
+      for (; i < n_iter; i += 4) quad(Seg1{}, i);
+    } else {
+      for (; i < n_iter; i += 4) quad(SegDyn{}, i);
     }
   } else if (idle) {
     for (int i = 0; i < n_iter; ++i) {

@@ -459,6 +459,46 @@ def time_burst(fn, burst, repeats=3):
     return float(np.median(times))
 
 
+def time_together(fns, burst, rounds=7, warm_s=0.5):
+    """Duration (ms) of one launch of each function in `fns` (name -> callable), measured
+    side by side: each is captured once into a HIP graph of `burst` back-to-back launches,
+    the graphs are replayed in turn for about warm_s seconds, then in each of `rounds`
+    rounds every graph is replayed once and timed with HIP events, in an order that
+    rotates from round to round; the median over the rounds, divided by `burst`.
+    Functions compared in one call see the same clock whatever their order, which
+    timing them one after another does not give."""
+    import torch
+    graphs = {}
+    for name, fn in fns.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(burst):
+                fn()
+        graphs[name] = graph
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for graph in graphs.values():
+            graph.replay()
+        torch.cuda.synchronize()
+    names = list(graphs)
+    times = {n: [] for n in names}
+    for r in range(rounds):
+        k = r % len(names)
+        for n in names[k:] + names[:k]:
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            graphs[n].replay()
+            e.record()
+            torch.cuda.synchronize()
+            times[n].append(s.elapsed_time(e) / burst)
+    return {n: float(np.median(t)) for n, t in times.items()}
+
+
 def kernel_bursts(path, only=None, burst=KERNEL_BURST):
     """Average duration (ms) of each kernel of the step over `burst` back-to-back launches."""
     snd = path.send()
@@ -522,11 +562,10 @@ def ulysses_chain(path, burst=10):
     step_fused()
     torch.cuda.synchronize()
     same = bool(torch.equal(send_unfused(), snd_f))
-    res = {"unfused_step_us": time_burst(step_unfused, burst) * 1e3,
-           "fused_step_us": time_burst(step_fused, burst) * 1e3,
-           "unfused_attn_us": time_burst(attn_unfused, burst) * 1e3,
-           "fused_attn_us": time_burst(attn_fused, burst) * 1e3,
-           "fused_send_equals_unfused": same}
+    t = time_together({"unfused_step": step_unfused, "fused_step": step_fused,
+                       "unfused_attn": attn_unfused, "fused_attn": attn_fused}, burst)
+    res = {f"{n}_us": ms * 1e3 for n, ms in t.items()}
+    res["fused_send_equals_unfused"] = same
     res["step_speedup"] = res["unfused_step_us"] / res["fused_step_us"]
     return res
 
@@ -573,11 +612,10 @@ def ulysses_2d_chain(path, burst=5):
     step_fused()
     torch.cuda.synchronize()
     diff = float((path.send().float() - snd_f.float()).abs().max())
-    res = {"unfused_step_us": time_burst(step_unfused, burst) * 1e3,
-           "fused_step_us": time_burst(step_fused, burst) * 1e3,
-           "unfused_attn_us": time_burst(path.attn, burst) * 1e3,
-           "fused_attn_us": time_burst(attn_fused, burst) * 1e3,
-           "max_abs_diff_fused_vs_unfused": diff}
+    t = time_together({"unfused_step": step_unfused, "fused_step": step_fused,
+                       "unfused_attn": path.attn, "fused_attn": attn_fused}, burst)
+    res = {f"{n}_us": ms * 1e3 for n, ms in t.items()}
+    res["max_abs_diff_fused_vs_unfused"] = diff
     res["step_speedup"] = res["unfused_step_us"] / res["fused_step_us"]
     return res
 
@@ -621,6 +659,11 @@ def chunked_kv(path, burst=10):
         cp.cp_attn_partial_accum(q, ks[W - 1], vs[W - 1], st_o, st_l, ms[W - 1], scale=path.scale,
                                  final=True, out=out_acc)
 
+    out_dense = torch.empty_like(q)
+
+    def dense_call():
+        cp.cp_attn_localq_globalkv(q, k, v, path.mask, scale=path.scale, out=out_dense)
+
     # the results, compared with a dense call into a tensor of their own
     partials()
     merge()
@@ -629,15 +672,20 @@ def chunked_kv(path, burst=10):
     torch.cuda.synchronize()
     diff = (out.float() - dense.float()).abs()
     diff_acc = (out_acc.float() - dense.float()).abs()
-    res = {"chunks": W, "partials_us": time_burst(partials, burst) * 1e3,
-           "merge_us": time_burst(merge, burst) * 1e3,
+    t = time_together({"partials": partials, "merge": merge, "accumulate": accumulate,
+                       "last_chunk_accumulate": last_accumulate, "dense": dense_call}, burst)
+    res = {"chunks": W, "partials_us": t["partials"] * 1e3, "merge_us": t["merge"] * 1e3,
            "merge_bytes": int(o_parts.numel() * 4 + lses.numel() * 4 + out.numel() * 2),
            "max_abs_diff_vs_dense": float(diff.max()),
            "elements_differing_from_dense": int((diff > 0).sum()),
-           "accumulate_us": time_burst(accumulate, burst) * 1e3,
-           "last_chunk_accumulate_us": time_burst(last_accumulate, burst) * 1e3,
-           "accumulate_max_abs_diff_vs_dense": float(diff_acc.max())}
+           "accumulate_us": t["accumulate"] * 1e3,
+           "last_chunk_accumulate_us": t["last_chunk_accumulate"] * 1e3,
+           "accumulate_max_abs_diff_vs_dense": float(diff_acc.max()),
+           "dense_us": t["dense"] * 1e3}
     res["merge_GBps"] = res["merge_bytes"] / (res["merge_us"] * 1e-6) / 1e9
+    res["total_us"] = res["partials_us"] + res["merge_us"]
+    res["total_over_dense"] = res["total_us"] / res["dense_us"]
+    res["accumulate_over_dense"] = res["accumulate_us"] / res["dense_us"]
     return res
 
 
@@ -652,15 +700,13 @@ def joint_segments(path, burst=10):
     ki, vi = k[:, :S_img].contiguous(), v[:, :S_img].contiguous()
     kj, vj, jm = k[:, S_img:].contiguous(), v[:, S_img:].contiguous(), m[:, S_img:].contiguous()
     out = torch.empty_like(path.attn_q)
-    res = {}
+    fns = {}
     for name, front in (("rear", False), ("front", True)):
         def call(front=front):
             cp.cp_attn_joint(path.attn_q, ki, vi, kj, vj, None, jm, joint_front=front, scale=path.scale, out=out)
-        call()
-        torch.cuda.synchronize()
-        res[f"{name}_us"] = time_burst(call, burst) * 1e3
-    res["concatenated_us"] = time_burst(path.attn, burst) * 1e3
-    return res
+        fns[name] = call
+    fns["concatenated"] = path.attn
+    return {f"{n}_us": ms * 1e3 for n, ms in time_together(fns, burst).items()}
 
 
 def packed_varlen(path, n_docs=4, burst=10):
@@ -1170,13 +1216,8 @@ def measure_config(path, args, step_fn):
                      "same FLOPs as the local-Q/global-KV share")
         rec["ulysses_fused"] = u
         c = chunked_kv(path)
-        c["total_us"] = c["partials_us"] + c["merge_us"]
-        c["dense_us"] = kern["attn"]["us"] if "attn" in kern else None
-        if c["dense_us"]:
-            c["total_over_dense"] = c["total_us"] / c["dense_us"]
-            c["accumulate_over_dense"] = c["accumulate_us"] / c["dense_us"]
         c["note"] = ("local-Q/global-KV share with K/V in W chunks: W partial attentions "
-                     "(fp32 O + lse) and one merge, against the dense call")
+                     "(fp32 O + lse) and one merge, against the dense call timed beside them")
         rec["chunked_kv"] = c
     if args.only is None and path.two_d and not args.no_extras:
         u = ulysses_2d_chain(path)

@@ -808,46 +808,46 @@ def uaa_compare(seqs, heads=14, D=128, seed=1240):
 
         u_step()
         u_fused_step()
-        torch.cuda.synchronize()
-        burst = 3 if S > 40000 else 5
-        rec["uaa_usp4"] = {"heads_per_rank": Hl, "padded_heads": H_pad - heads,
-                           "attn_us": time_burst(u_attn, burst) * 1e3,
-                           "step_us": time_burst(u_step, burst) * 1e3,
-                           "fused_step_us": time_burst(u_fused_step, burst) * 1e3,
-                           "attn_flops": 4 * Hl * S * S * D}
-        del x, st, recv, hs, o, snd_f, peers, rcv, out
-        # ---- cp2usp2: Ulysses 2 inside an AllGather-KV pair
+        # ---- cp2usp2: Ulysses 2 inside an AllGather-KV pair (buffers of its own, so that
+        # both layouts are timed side by side)
         U = 2
         Hu = heads // U
-        x = [randn(1, Sl, heads, D) for _ in range(3)]
-        st = [torch.empty((U, Sl, Hu, 3 * D), dtype=torch.bfloat16, device=dev) for _ in range(U)]
-        cp.cp_pack_qkv_dst_major(*[randn(1, Sl, heads, D) for _ in range(3)], U, staging=st[1])
-        recv = torch.empty_like(st[0])
+        cx = [randn(1, Sl, heads, D) for _ in range(3)]
+        cst = [torch.empty((U, Sl, Hu, 3 * D), dtype=torch.bfloat16, device=dev) for _ in range(U)]
+        cp.cp_pack_qkv_dst_major(*[randn(1, Sl, heads, D) for _ in range(3)], U, staging=cst[1])
+        crecv = torch.empty_like(cst[0])
         q_hs = torch.empty((1, U * Sl, Hu, D), dtype=torch.bfloat16, device=dev)
         k_glob, v_glob = randn(1, S, Hu, D), randn(1, S, Hu, D)
         k_reg0, v_reg0 = k_glob[:, :U * Sl], v_glob[:, :U * Sl]
-        o = torch.empty((1, U * Sl, Hu, D), dtype=torch.bfloat16, device=dev)
-        peers = [None, randn(U, 1, Sl, Hu, D)]
-        rcv = torch.empty((U, 1, Sl, Hu, D), dtype=torch.bfloat16, device=dev)
-        out = torch.empty((1, Sl, heads, D), dtype=torch.bfloat16, device=dev)
+        co = torch.empty((1, U * Sl, Hu, D), dtype=torch.bfloat16, device=dev)
+        cpeers = [None, randn(U, 1, Sl, Hu, D)]
+        crcv = torch.empty((U, 1, Sl, Hu, D), dtype=torch.bfloat16, device=dev)
+        cout = torch.empty((1, Sl, heads, D), dtype=torch.bfloat16, device=dev)
 
         def c_attn():
-            cp.cp_attn_localq_globalkv(q_hs, k_glob, v_glob, scale=scale, out=o)
+            cp.cp_attn_localq_globalkv(q_hs, k_glob, v_glob, scale=scale, out=co)
 
         def c_step():
-            cp.cp_pack_qkv_dst_major(*x, U, staging=st[0])
-            cp.cp_sim_exchange(st, 0, recv=recv)
-            cp.cp_unpack_head_sharded(recv, 1, U, out=(q_hs, k_reg0, v_reg0))
+            cp.cp_pack_qkv_dst_major(*cx, U, staging=cst[0])
+            cp.cp_sim_exchange(cst, 0, recv=crecv)
+            cp.cp_unpack_head_sharded(crecv, 1, U, out=(q_hs, k_reg0, v_reg0))
             c_attn()
-            cp.cp_sim_exchange([o.view(U, 1, Sl, Hu, D)] + peers[1:], 0, recv=rcv)
-            cp.cp_output_reverse(1, rcv, U, 1, out=out)
+            cp.cp_sim_exchange([co.view(U, 1, Sl, Hu, D)] + cpeers[1:], 0, recv=crcv)
+            cp.cp_output_reverse(1, crcv, U, 1, out=cout)
 
         c_step()
         torch.cuda.synchronize()
-        rec["cp2usp2"] = {"heads_per_rank": Hu, "attn_us": time_burst(c_attn, burst) * 1e3,
-                          "step_us": time_burst(c_step, burst) * 1e3,
+        burst = 3 if S > 40000 else 5
+        t = time_together({"u_attn": u_attn, "u_step": u_step, "u_fused_step": u_fused_step,
+                           "c_attn": c_attn, "c_step": c_step}, burst)
+        rec["uaa_usp4"] = {"heads_per_rank": Hl, "padded_heads": H_pad - heads,
+                           "attn_us": t["u_attn"] * 1e3, "step_us": t["u_step"] * 1e3,
+                           "fused_step_us": t["u_fused_step"] * 1e3,
+                           "attn_flops": 4 * Hl * S * S * D}
+        rec["cp2usp2"] = {"heads_per_rank": Hu, "attn_us": t["c_attn"] * 1e3, "step_us": t["c_step"] * 1e3,
                           "attn_flops": 4 * Hu * (S // 2) * S * D}
-        del x, st, recv, q_hs, k_glob, v_glob, k_reg0, v_reg0, o, peers, rcv, out
+        del x, st, recv, hs, o, snd_f, peers, rcv, out
+        del cx, cst, crecv, q_hs, k_glob, v_glob, k_reg0, v_reg0, co, cpeers, crcv, cout
         torch.cuda.empty_cache()
         u, c = rec["uaa_usp4"], rec["cp2usp2"]
         rec["attn_reduction"] = 1.0 - c["attn_us"] / u["attn_us"]

@@ -518,6 +518,8 @@ def test_chunked_kv_arrival_full_size_whole(gu):
     (2, 2, 129, 500, 200, 128, False, False, False),  # no masks
     (1, 2, 64, 300, 0, 64, False, True, False),       # no joint tokens
     (1, 1, 256, 4096, 77, 128, True, False, True),    # 2 query blocks: split-KV over two segments
+    (1, 64, 1024, 300, 1, 128, True, False, True),    # 256-row blocks: one joint key, then the image keys
+    (1, 64, 1000, 64, 333, 128, False, True, True),   # 256-row blocks: a one-tile image segment, then the joint
 ])
 def test_joint_segments_match_oracle(gu, B, H, Sq, S_img, T, D, front, im_on, jm_on):
     import context_attention_diffusion_amd as cp
